@@ -1,0 +1,174 @@
+"""CPU oracle for the reproducible operations (ctypes over ``librepro_oracle.so``).
+
+TEST INFRASTRUCTURE ONLY: the tests, the smoke check and the benchmark's
+CPU-baseline leg use it; the GPU library never does.  Every function below
+only marshals numpy arrays into the C oracle, which holds all the arithmetic
+(see ``repro_oracle.c`` for the definitions and their sources on the pages).
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_LIB_PATH = os.path.join(_HERE, "librepro_oracle.so")
+_lib = None
+
+OP_ADD, OP_SUB, OP_MUL, OP_DIV, OP_SQRT = range(5)
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        if not os.path.exists(_LIB_PATH):
+            from . import build as _b
+            _b.build()
+        lib = ctypes.CDLL(_LIB_PATH)
+        i64, vp, i32, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
+        lib.oracle_fp32_ops.argtypes = [ctypes.c_int, vp, vp, vp, i64]
+        lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.oracle_tree_reduce.argtypes = [vp, i32, i64, vp, i32, vp]
+        lib.oracle_adamw_scalars.argtypes = [f32, f32, i64, vp]
+        lib.oracle_adamw.argtypes = [vp, vp, i64, f32, f32, f32, f32, f32, i64]
+        lib.oracle_blake2b.argtypes = [vp, i64, ctypes.c_int, vp, vp]
+        lib.oracle_state_hash_leaves.argtypes = [vp, i64, i64, i64, vp]
+        lib.oracle_state_hash.argtypes = [vp, i64, vp]
+        lib.oracle_spec_version.restype = ctypes.c_char_p
+        for name in ("oracle_fp32_ops", "oracle_gemm", "oracle_tree_reduce", "oracle_adamw_scalars",
+                     "oracle_adamw", "oracle_blake2b", "oracle_state_hash_leaves", "oracle_state_hash"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+class swap_library:
+    """Context manager: route every call to another build of the oracle
+    (used only by the mutation tests, which compile deliberately broken
+    copies of ``repro_oracle.c`` to show the pins catch them)."""
+
+    def __init__(self, path: str):
+        self.path = path
+
+    def __enter__(self):
+        global _lib
+        _load()
+        self.saved = _lib
+        _lib = None
+        saved_path = globals()["_LIB_PATH"]
+        globals()["_LIB_PATH"] = self.path
+        try:
+            _load()
+        finally:
+            globals()["_LIB_PATH"] = saved_path
+        return self
+
+    def __exit__(self, *exc):
+        global _lib
+        _lib = self.saved
+        return False
+
+
+def _check(rc: int, what: str):
+    if rc != 0:
+        raise ValueError(f"{what}: oracle returned {rc}")
+
+
+def _f32(x) -> np.ndarray:
+    return np.ascontiguousarray(x, dtype=np.float32)
+
+
+def spec_version() -> str:
+    return _load().oracle_spec_version().decode()
+
+
+def fp32_op(op: int, a, b=None) -> np.ndarray:
+    """One contract operation per element (0 add, 1 sub, 2 mul, 3 div, 4 sqrt)."""
+    a = _f32(a)
+    b = _f32(a if b is None else b)
+    assert a.shape == b.shape
+    out = np.empty_like(a)
+    _check(_load().oracle_fp32_ops(op, a.ctypes.data, b.ctypes.data, out.ctypes.data, a.size), "fp32_ops")
+    return out
+
+
+def gemm(A, B, trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
+    """C = op(A) @ op(B) with one ascending-k unfused chain per output."""
+    A = _f32(A)
+    B = _f32(B)
+    M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
+    K2, N = (B.shape[1], B.shape[0]) if trans_b else B.shape
+    assert K == K2, "inner dimensions differ"
+    C = np.empty((M, N), dtype=np.float32)
+    lda = A.shape[1] if A.ndim == 2 and A.shape[1] > 0 else 1
+    ldb = B.shape[1] if B.ndim == 2 and B.shape[1] > 0 else 1
+    _check(_load().oracle_gemm(int(trans_a), int(trans_b), M, N, K, A.ctypes.data, lda, B.ctypes.data,
+                               ldb, C.ctypes.data, max(N, 1)), "gemm")
+    return C
+
+
+def tree_reduce(replicas, average: bool = True, return_resident: bool = False):
+    reps = [_f32(r).reshape(-1) for r in replicas]
+    R = len(reps)
+    n = reps[0].size if R else 0
+    assert all(r.size == n for r in reps)
+    ptrs = (ctypes.c_void_p * max(R, 1))(*[r.ctypes.data for r in reps])
+    out = np.empty(n, dtype=np.float32)
+    resident = ctypes.c_int32(0)
+    _check(_load().oracle_tree_reduce(ctypes.cast(ptrs, ctypes.c_void_p), R, n, out.ctypes.data,
+                                      int(average), ctypes.addressof(resident)), "tree_reduce")
+    return (out, resident.value) if return_resident else out
+
+
+def adamw_scalars(beta1: float, beta2: float, step: int) -> np.ndarray:
+    """The host scalars (c1, c2, r1, r2) as binary32."""
+    out = np.zeros(4, dtype=np.float32)
+    _check(_load().oracle_adamw_scalars(beta1, beta2, step, out.ctypes.data), "adamw_scalars")
+    return out
+
+
+def adamw(state, grad, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float,
+          step: int) -> np.ndarray:
+    """Returns the updated flat [w | m | v] state (the input is not modified)."""
+    st = np.array(state, dtype=np.float32, copy=True).reshape(-1)
+    g = _f32(grad).reshape(-1)
+    n = g.size
+    assert st.size == 3 * n
+    _check(_load().oracle_adamw(st.ctypes.data, g.ctypes.data, n, lr, beta1, beta2, eps, weight_decay,
+                                step), "adamw")
+    return st
+
+
+def adamw_inplace(state: np.ndarray, grad: np.ndarray, lr, beta1, beta2, eps, weight_decay, step):
+    assert state.dtype == np.float32 and state.flags.c_contiguous
+    g = _f32(grad).reshape(-1)
+    assert state.size == 3 * g.size
+    _check(_load().oracle_adamw(state.ctypes.data, g.ctypes.data, g.size, lr, beta1, beta2, eps,
+                                weight_decay, step), "adamw")
+
+
+def blake2b(data: bytes, digest_size: int = 64, person: bytes = b"") -> bytes:
+    buf = np.frombuffer(bytes(data), dtype=np.uint8) if data else np.zeros(1, dtype=np.uint8)
+    p = np.zeros(16, dtype=np.uint8)
+    p[:len(person)] = np.frombuffer(person, dtype=np.uint8)
+    out = np.zeros(64, dtype=np.uint8)
+    _check(_load().oracle_blake2b(buf.ctypes.data, len(data), digest_size, p.ctypes.data, out.ctypes.data),
+           "blake2b")
+    return out[:digest_size].tobytes()
+
+
+def state_hash(words) -> bytes:
+    w = _f32(words).reshape(-1)
+    out = np.zeros(32, dtype=np.uint8)
+    ptr = w.ctypes.data if w.size else np.zeros(1, np.float32).ctypes.data
+    _check(_load().oracle_state_hash(ptr, w.size, out.ctypes.data), "state_hash")
+    return out.tobytes()
+
+
+def state_hash_leaves(words, leaf0: int, count: int) -> np.ndarray:
+    w = _f32(words).reshape(-1)
+    out = np.zeros((count, 32), dtype=np.uint8)
+    ptr = w.ctypes.data if w.size else np.zeros(1, np.float32).ctypes.data
+    _check(_load().oracle_state_hash_leaves(ptr, w.size, leaf0, count, out.ctypes.data), "state_hash_leaves")
+    return out

@@ -1,0 +1,85 @@
+"""The oracle's pins are not vacuous: each plausible mistake, planted in a copy
+of the oracle source and compiled on the CPU, makes at least one pin fail.
+
+Nothing here touches the GPU library or the committed oracle build.
+"""
+import os
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from oracle import build as oracle_build
+
+import test_oracle_adamw as T_ADAMW
+import test_oracle_fp32 as T_FP32
+import test_oracle_gemm as T_GEMM
+import test_oracle_hash as T_HASH
+import test_oracle_tree_reduce as T_TREE
+
+SRC = oracle_build.SRC
+
+# (name, text to find, replacement, pins that must fail)
+MUTATIONS = [
+    ("gemm_descending_k", "for (int64_t k = 0; k < K; ++k)", "for (int64_t k = K - 1; k >= 0; --k)",
+     [T_GEMM.test_ascending_k_order_witness]),
+    ("gemm_fused_mac", "acc = f_add(acc, f_mul(a, b));", "acc = flush(fmaf(flush(a), flush(b), acc));",
+     [T_GEMM.test_unfused_multiply_add_witness]),
+    ("gemm_transposed_a", "float a = trans_a ? A[k * lda + i] : A[i * lda + k];",
+     "float a = trans_a ? A[i * lda + k] : A[k * lda + i];",
+     [lambda: T_GEMM.test_exact_integer_products(0, 0, 3, 5, 7)]),
+    ("gemm_dropped_last_term", "for (int64_t k = 0; k < K; ++k)", "for (int64_t k = 0; k + 1 < K; ++k)",
+     [lambda: T_GEMM.test_exact_integer_products(0, 0, 17, 9, 64), T_GEMM.test_within_recursive_summation_error_bound]),
+    ("tree_result_largest_first",
+     "float* acc = f->stack[f->depth - 1].part;\n    for (int s = f->depth - 2; s >= 0; --s) {",
+     "float* acc = f->stack[0].part;\n    for (int s = 1; s < f->depth; ++s) {",
+     [T_TREE.test_non_power_of_two_remainder_folded_first]),
+    ("tree_sequential_fold", "while (f->depth > 0 && f->stack[f->depth - 1].level == level)", "while (0)",
+     [lambda: T_TREE.test_treefold_equals_recursive_doubling(8)]),
+    ("tree_divides", "out[i] = f_mul(acc[i], rR);", "out[i] = f_div(acc[i], (float)R);",
+     [lambda: T_TREE.test_average_is_reciprocal_multiply_not_division(3)]),
+    ("adamw_eps_inside_root", "const float d = f_add(sq, eps);", "const float d = f_sqrt(f_add(vh, eps));",
+     [T_ADAMW.test_first_step_closed_form, T_ADAMW.test_constant_gradient_trajectory]),
+    ("adamw_no_bias_correction_m", "const float mh = f_mul(mn, s.r1);", "const float mh = mn;",
+     [T_ADAMW.test_constant_gradient_trajectory, T_ADAMW.test_dyadic_case_is_exact]),
+    ("adamw_wd_sign", "const float z = f_add(u, y);", "const float z = f_sub(u, y);",
+     [T_ADAMW.test_first_step_closed_form, T_ADAMW.test_dyadic_case_is_exact]),
+    ("adamw_moments_swapped", "Mo[i] = mn;\n        V[i] = vn;", "Mo[i] = vn;\n        V[i] = mn;",
+     [T_ADAMW.test_dyadic_case_is_exact]),
+    ("adamw_beta_power_off_by_one", "for (int64_t t = 1; t < step; ++t)", "for (int64_t t = 0; t < step; ++t)",
+     [T_ADAMW.test_dyadic_case_is_exact, T_ADAMW.test_host_scalars]),
+    ("hash_inner_depth", "sh_node(level + 32 * c0, (size_t)nc * 32, (uint64_t)j, depth,",
+     "sh_node(level + 32 * c0, (size_t)nc * 32, (uint64_t)j, 1,", [lambda: T_HASH.test_tree_mode_matches_hashlib(128 * 128 * 1024 + 5)]),
+    ("hash_no_last_leaf_flag", "(uint64_t)i, 0, i == leaves - 1,", "(uint64_t)i, 0, 0,",
+     [lambda: T_HASH.test_tree_mode_matches_hashlib(1025)]),
+    ("blake2b_rotation", "v[b] = rotr64(v[b] ^ v[c], 63);", "v[b] = rotr64(v[b] ^ v[c], 62);",
+     [T_HASH.test_rfc7693_known_answer]),
+    ("no_flush", "if (fpclassify(x) == FP_SUBNORMAL) return copysignf(0.0f, x);", "",
+     [T_FP32.test_subnormal_results_flush_with_sign]),
+    ("hardware_ftz_daz", "_mm_setcsr((e.saved & ~(0x6000u | 0x8000u | 0x0040u)) | 0x1F80u);",
+     "_mm_setcsr((e.saved & ~0x6000u) | 0x1F80u | 0x8000u | 0x0040u);",
+     [T_FP32.test_flush_decision_follows_the_rounded_result]),
+]
+
+
+@pytest.fixture(scope="module")
+def workdir():
+    with tempfile.TemporaryDirectory() as d:
+        yield d
+
+
+@pytest.mark.parametrize("name,find,repl,pins", MUTATIONS, ids=[m[0] for m in MUTATIONS])
+def test_planted_mistake_is_caught(workdir, name, find, repl, pins):
+    src = open(SRC).read()
+    assert src.count(find) >= 1, f"mutation anchor not found: {find!r}"
+    mutated = src.replace(find, repl, 1)
+    cpath = os.path.join(workdir, f"{name}.c")
+    with open(cpath, "w") as fh:
+        fh.write(mutated)
+    lib = os.path.join(workdir, f"lib{name}.so")
+    subprocess.run(["gcc", *oracle_build.FLAGS, cpath, "-o", lib, "-lm"], check=True)
+    with oracle.swap_library(lib):
+        for pin in pins:
+            with pytest.raises(AssertionError):
+                pin()
