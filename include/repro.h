@@ -1,0 +1,192 @@
+/*
+ * repro.h - C ABI of librepro.so: bitwise-reproducible training-step
+ * operations for AMD Instinct MI355X (gfx950).
+ *
+ * The operations are the order-fixed "reproducible operations" of
+ * "OPEN-1B: A Fully Auditable Training Run" (Gensyn):
+ *   - section 2 and 2.1 with Table 1: results are equal bit for bit, with one
+ *     fixed reduction order, multiply and add unfused, and subnormal
+ *     operands and results flushed to zero;
+ *   - Appendix A.1 with Algorithm 2 (TreeFold) and Appendix A.3 (an average is
+ *     a multiply by a host-computed reciprocal);
+ *   - section 3.2 "Optimizer" and "Optimizer-state precision" (fused FP32
+ *     AdamW with decoupled weight decay);
+ *   - Appendix B and Figure 11 (a BLAKE2b state hash per step).
+ *
+ * Numeric contract shared by every call: IEEE 754 binary32, round to
+ * nearest even, no fused multiply-add.  A subnormal operand reads as a zero
+ * of the same sign.  A result whose IEEE (gradual-underflow) rounding is
+ * subnormal becomes a zero of the same sign.  Division and square root are
+ * correctly rounded.  Inputs are assumed finite.
+ *
+ * Determinism promise: output bits depend only on the input bits and the
+ * arguments, never on the stream, the launch configuration (the *_variant
+ * entry points select alternative launch shapes that must give the same
+ * bits), the device, or the process.
+ *
+ * Conventions for every call:
+ *   - Pointers named "device" point to device memory (a hipMalloc'd
+ *     allocation, e.g. a torch tensor on a ROCm device) and must be aligned
+ *     to 4 bytes.  16-byte alignment enables the vectorised kernels; other
+ *     alignments take a slower path with identical results.
+ *   - The caller owns every buffer.  The library allocates nothing and keeps
+ *     no global state; calls are thread-safe.
+ *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
+ *     Every call only enqueues work on it and returns without waiting.
+ *   - Return value: REPRO_OK (0) or a negative REPRO_E* code.  On an error
+ *     nothing has been enqueued, except REPRO_EDEVICE, which reports a HIP
+ *     launch failure (hipGetLastError) after the launch.
+ */
+#ifndef REPRO_H
+#define REPRO_H
+
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define REPRO_OK 0
+#define REPRO_EINVAL -1 /* null pointer, negative size, bad flag, R out of range, ld too small, step < 1 */
+#define REPRO_EALIGN -2 /* a device pointer is not 4-byte aligned */
+#define REPRO_EDEVICE -3 /* HIP launch or runtime error */
+#define REPRO_ESPACE -4 /* hash workspace too small */
+
+#define REPRO_MAX_REPLICAS 64
+
+/* "repro-spec-1": names the orders, the constants and the hash parameters
+ * below.  A change to any of them changes this string. */
+const char* repro_spec_version(void);
+
+/* Static description of a status code. */
+const char* repro_strerror(int status);
+
+/*
+ * repro_gemm: C = op(A) * op(B), binary32, row-major.
+ *
+ * Paper section 2.1 "Reduction order" (one fixed order for every sum in a
+ * matrix multiply) and "Fused multiply-add" (unfused); section 6 item 1.
+ * Each C[i][j] is one serial chain: acc = +0, then for k = 0, 1, ..., K-1
+ * in ascending order acc = fl(acc + fl(opA[i][k] * opB[k][j])).  The kernel
+ * tiles only over outputs and never splits k.
+ *
+ *   op(A) is M x K: A[i*lda + k], or A[k*lda + i] when trans_a != 0
+ *   op(B) is K x N: B[k*ldb + j], or B[j*ldb + k] when trans_b != 0
+ *   C[i*ldc + j], M x N.
+ * Requirements: M, N, K >= 0; ldc >= N; when K > 0, lda >= (trans_a ? M : K)
+ * and ldb >= (trans_b ? K : N).  A, B, C are device pointers; C must not
+ * overlap A or B.  M == 0 or N == 0: nothing to do.  K == 0: C = +0.
+ */
+int repro_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+               const float* B, int64_t ldb, float* C, int64_t ldc, void* stream);
+
+/* As repro_gemm with an explicit kernel variant: 0 is the default; 1 uses
+ * scalar global loads; 2 uses a 64x64 output tile.  All variants return the
+ * same bits; they exist to test that claim. */
+int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A,
+                       int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant,
+                       void* stream);
+
+/*
+ * repro_tree_reduce: out[i] = Fold(x_0[i], ..., x_{R-1}[i]) (times fl(1/R)).
+ *
+ * Paper Appendix A.1 with Algorithm 2: TreeFold, the binary-carry fold that
+ * reproduces the recursive-doubling all-reduce order over replicas.  Push
+ * combines equal-size blocks with the lower replicas on the left; Result
+ * starts from the smallest remaining block and adds the larger ones in turn,
+ * so for R = 8 the sum is ((x0+x1)+(x2+x3))+((x4+x5)+(x6+x7)) and for
+ * R = 7 it is (x6+(x4+x5))+((x0+x1)+(x2+x3)).  Appendix A.3: when average
+ * is nonzero the fold is multiplied by rR = fl(1/R), a binary32 reciprocal
+ * computed on the host; it is never a division.
+ *
+ *   replicas: HOST array of R device pointers, each to n floats (replica
+ *             gradient buffers in replica order 0..R-1).  The array itself
+ *             is read during the call only.
+ *   R:        1 <= R <= REPRO_MAX_REPLICAS.
+ *   out:      device pointer to n floats.  It may be one of the replicas
+ *             (each element is read before it is written) but must not
+ *             partially overlap any of them.
+ *   average:  0 = plain fold, nonzero = fold * fl(1/R).
+ * n == 0: nothing to do.
+ */
+int repro_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float* out, int32_t average,
+                      void* stream);
+
+/* Variant 0 default (16-byte vectors, 256 threads); 1 scalar elements;
+ * 2 16-byte vectors, 64 threads and a grid-stride loop over a small grid. */
+int repro_tree_reduce_variant(const float* const* replicas, int32_t R, int64_t n, float* out,
+                              int32_t average, int32_t variant, void* stream);
+
+/*
+ * repro_adamw: one fused AdamW step, in place, on the flat binary32 state.
+ *
+ * Paper section 3.2 "Optimizer" (AdamW, decoupled weight decay, a
+ * bitwise-reproducible fused kernel) and "Optimizer-state precision" (FP32
+ * moments); the checkpoint page's file format gives the flat [w | m | v]
+ * layout.  Host scalars (binary32, same contract): c1 = 1 - beta1,
+ * c2 = 1 - beta2, p = beta^step by step-1 serial multiplies, r1 = 1/(1 - p1),
+ * r2 = 1/(1 - p2) (Appendix A.3's reciprocal rule applied to the bias
+ * corrections).  Per element, in this order, each step one rounding:
+ *   m1 = beta1*m   m2 = c1*g   m' = m1 + m2
+ *   q = g*g        v1 = beta2*v  v2 = c2*q  v' = v1 + v2
+ *   mh = m'*r1     vh = v'*r2
+ *   s = sqrt(vh)   d = s + eps   u = mh / d
+ *   y = wd*w       z = u + y     t = lr*z   w' = w - t
+ *
+ *   state: device pointer to 3n floats: w = state[0..n), m = state[n..2n),
+ *          v = state[2n..3n).  Updated in place (w', m', v').
+ *   grad:  device pointer to n floats; must not overlap state.
+ *   step:  the step being taken, >= 1.
+ * n == 0: nothing to do.
+ */
+int repro_adamw(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
+                float weight_decay, int64_t step, void* stream);
+
+/* Variant 0 default (16-byte vectors); 1 scalar elements. */
+int repro_adamw_variant(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2,
+                        float eps, float weight_decay, int64_t step, int32_t variant, void* stream);
+
+/*
+ * repro_state_hash: 32-byte BLAKE2b tree digest of n_words binary32 words.
+ *
+ * Paper Appendix B (a canonical per-step state hash) and Figure 11 (the hash
+ * is BLAKE2b); section 3.2 (state hashed in FP32).  BLAKE2b as RFC 7693, in
+ * the tree mode of the BLAKE2 paper (section 2.10) with digest length 32,
+ * fanout 16, depth 255, leaf length 4096, inner length 32 and
+ * personalisation "repro_state_v1" (zero-padded to 16 bytes), over the
+ * little-endian bytes of the words:
+ *   level 0: leaves of 4096 bytes (the last may be shorter; no words = one
+ *            empty leaf), leaf i at node offset i, node depth 0;
+ *   level d >= 1: node j hashes the concatenated digests of children
+ *            16j .. 16j+15 of level d-1, node offset j, node depth d;
+ *   the last node of every level carries the last-node flag; levels are
+ *   added until one node remains, always at least one above the leaves.
+ * The root digest is the state hash.  Hash [w | m | v] by passing
+ * state and 3n.
+ *
+ *   words:      device pointer to n_words floats (n_words >= 0).
+ *   workspace:  device memory of at least
+ *               repro_state_hash_workspace_bytes(n_words) bytes, 16-byte
+ *               aligned, used for the digests of every level.
+ *   digest_out: device pointer to 32 bytes, written last.
+ */
+int64_t repro_state_hash_workspace_bytes(int64_t n_words);
+int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64_t ws_bytes,
+                     uint8_t* digest_out, void* stream);
+
+/*
+ * repro_fp32_ops: one contract operation per element, with the same device
+ * arithmetic the kernels use (diagnostic entry point for directed tests of
+ * the flush rule, division and square root).
+ *   op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (b ignored): the element-wise
+ *        arithmetic of repro_tree_reduce and repro_adamw;
+ *   op 5 mul, 6 add: the arithmetic of repro_gemm's multiply-accumulate.
+ * a, b, out: device pointers to n floats.
+ */
+int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* REPRO_H */

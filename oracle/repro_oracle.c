@@ -423,18 +423,18 @@ int oracle_blake2b(const uint8_t* in, int64_t len, int outlen, const uint8_t* pe
 }
 
 /* State hash: BLAKE2b tree mode over the little-endian bytes of the words.
- *   digest 32 bytes; fanout 128; depth 255; leaf length 4096; inner 32;
+ *   digest 32 bytes; fanout 16; depth 255; leaf length 4096; inner 32;
  *   personalisation "repro_state_v1" padded with zero bytes to 16.
  * Level 0: the bytes are cut into leaves of 4096 bytes (the last one may be
  * shorter; an empty input is one empty leaf).  Leaf i is hashed with node
  * offset i, node depth 0, and the last-node flag on the last leaf only.
  * Level d >= 1: node j hashes the concatenated 32-byte digests of children
- * 128j .. 128j+127 of level d-1, node offset j, node depth d, last-node flag
+ * 16j .. 16j+15 of level d-1, node offset j, node depth d, last-node flag
  * on the last node of the level.  Levels are added until one node is left;
  * there is always at least one level above the leaves.  That node is the
  * root and its digest is the state hash. */
 #define SH_LEAF 4096
-#define SH_FANOUT 128
+#define SH_FANOUT 16
 #define SH_DEPTH 255
 #define SH_INNER 32
 static const uint8_t SH_PERSONAL[16] = {'r', 'e', 'p', 'r', 'o', '_', 's', 't', 'a', 't', 'e', '_', 'v', '1', 0, 0};

@@ -4,7 +4,7 @@ OPEN-1B paper, Appendix B (a sharded canonical per-step state hash) and the
 legend of Figure 11 (the hash is BLAKE2b); section 3.2 "Optimizer-state
 precision" (state hashed in FP32).  The function is BLAKE2b of RFC 7693 in
 the tree mode of the BLAKE2 paper (section 2.10), with leaf 4096 bytes,
-fanout 128, depth 255, inner digests and output 32 bytes, personalisation
+fanout 16, depth 255, inner digests and output 32 bytes, personalisation
 "repro_state_v1", over the little-endian bytes of [w | m | v].
 
 Python's hashlib implements BLAKE2b with the same tree parameters
@@ -24,7 +24,7 @@ GOLDEN = os.path.join(os.path.dirname(__file__), "golden", "blake2b_rfc7693.txt"
 
 
 def _node(data, offset, depth, last):
-    return hashlib.blake2b(data, digest_size=32, fanout=128, depth=255, leaf_size=4096,
+    return hashlib.blake2b(data, digest_size=32, fanout=16, depth=255, leaf_size=4096,
                            node_offset=offset, node_depth=depth, inner_size=32, last_node=last,
                            person=PERSON).digest()
 
@@ -35,8 +35,8 @@ def _hashlib_tree(words):
     level = [_node(b[i * 4096:(i + 1) * 4096], i, 0, i == L - 1) for i in range(L)]
     depth = 1
     while True:
-        parents = -(-len(level) // 128)
-        level = [_node(b"".join(level[j * 128:(j + 1) * 128]), j, depth, j == parents - 1)
+        parents = -(-len(level) // 16)
+        level = [_node(b"".join(level[j * 16:(j + 1) * 16]), j, depth, j == parents - 1)
                  for j in range(parents)]
         depth += 1
         if len(level) == 1:
@@ -59,10 +59,10 @@ def test_sequential_mode_matches_hashlib():
 
 
 # Word counts: empty; one word; a partial leaf; exactly one leaf; one leaf and
-# a word; 33 leaves; exactly 128 leaves (one level above the leaves);
-# 129 leaves (two levels); 128*128 leaves + 5 words (three levels).
-@pytest.mark.parametrize("n", [0, 1, 1023, 1024, 1025, 33 * 1024, 128 * 1024, 128 * 1024 + 1,
-                               128 * 128 * 1024 + 5])
+# a word; 16 leaves (one level above the leaves); 17 leaves (two levels);
+# 33 leaves; 16*16 leaves + 5 words (three levels); 5000 leaves (four).
+@pytest.mark.parametrize("n", [0, 1, 1023, 1024, 1025, 16 * 1024, 16 * 1024 + 1, 33 * 1024,
+                               16 * 16 * 1024 + 5, 5000 * 1024])
 def test_tree_mode_matches_hashlib(n):
     w = np.random.default_rng(n).standard_normal(n).astype(np.float32)
     assert oracle.state_hash(w) == _hashlib_tree(w)
