@@ -20,12 +20,15 @@
  * file format) fixes the flat [w | m | v] order and beta2 = 0.999.
  * BLAKE2b itself follows RFC 7693 (Saarinen and Aumasson, 2015).
  *
- * Floating-point model.  The host's SSE unit computes each binary32 operation
- * in IEEE 754 round-to-nearest-even with gradual underflow (the MXCSR FTZ and
- * DAZ bits are cleared on entry).  The flush rule is then applied by hand:
- * a subnormal operand is read as a zero of the same sign, and a subnormal
- * (rounded) result is replaced by a zero of the same sign.  Build with
- * -ffp-contract=off so no multiply and add are ever fused.
+ * Floating-point model.  Section 2.1 has the processor path flush subnormals
+ * by turning on its FTZ and DAZ modes.  On this x86-64 host those are the
+ * MXCSR bits FTZ (15) and DAZ (6): every binary32 operation below runs on the
+ * SSE unit with round-to-nearest-even, a subnormal operand read as a zero of
+ * the same sign, and a result replaced by a zero of the same sign when it is
+ * tiny, i.e. when its value rounded to 24 significant bits with an unbounded
+ * exponent is below 2^-126 (Intel SDM vol. 1, "Numeric Underflow Exception"
+ * and "Flush-To-Zero").  Build with -ffp-contract=off so no multiply and add
+ * are ever fused.
  */
 #include <math.h>
 #include <stdint.h>
@@ -38,36 +41,34 @@
 #define ORACLE_ENOMEM -5
 
 /* ------------------------------------------------------------------------ */
-/* The binary32 contract: IEEE RNE operation, operands and result flushed.   */
+/* The binary32 contract: SSE operations under FTZ and DAZ.                  */
 
 typedef struct { unsigned int saved; } fpenv_t;
 
-static fpenv_t enter_ieee(void) {
+static fpenv_t enter_contract(void) {
     fpenv_t e;
     e.saved = _mm_getcsr();
-    /* RNE (RC = 00), FTZ (bit 15) and DAZ (bit 6) off, all exceptions masked. */
-    _mm_setcsr((e.saved & ~(0x6000u | 0x8000u | 0x0040u)) | 0x1F80u);
+    /* RNE (RC = 00), FTZ (bit 15) and DAZ (bit 6) on, all exceptions masked. */
+    _mm_setcsr((e.saved & ~0x6000u) | 0x8000u | 0x0040u | 0x1F80u);
     return e;
 }
 
-static void leave_ieee(fpenv_t e) { _mm_setcsr(e.saved); }
+static void leave_contract(fpenv_t e) { _mm_setcsr(e.saved); }
 
-static float flush(float x) {
-    if (fpclassify(x) == FP_SUBNORMAL) return copysignf(0.0f, x);
-    return x;
-}
-
-static float f_add(float a, float b) { return flush(flush(a) + flush(b)); }
-static float f_sub(float a, float b) { return flush(flush(a) - flush(b)); }
-static float f_mul(float a, float b) { return flush(flush(a) * flush(b)); }
-static float f_div(float a, float b) { return flush(flush(a) / flush(b)); }
-static float f_sqrt(float a) { return flush(sqrtf(flush(a))); }
+/* One binary32 operation each; the control register does the flushing.
+ * (-frounding-math keeps the compiler from folding any of them at build
+ * time, where the run-time mode would not apply.) */
+static float f_add(float a, float b) { return a + b; }
+static float f_sub(float a, float b) { return a - b; }
+static float f_mul(float a, float b) { return a * b; }
+static float f_div(float a, float b) { return a / b; }
+static float f_sqrt(float a) { return sqrtf(a); }
 
 /* Single contract operations, exported for the directed tests.
  * op: 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (b ignored). */
 int oracle_fp32_ops(int op, const float* a, const float* b, float* out, int64_t n) {
     if (n < 0 || op < 0 || op > 4) return ORACLE_EINVAL;
-    fpenv_t e = enter_ieee();
+    fpenv_t e = enter_contract();
     for (int64_t i = 0; i < n; ++i) {
         switch (op) {
         case 0: out[i] = f_add(a[i], b[i]); break;
@@ -77,7 +78,7 @@ int oracle_fp32_ops(int op, const float* a, const float* b, float* out, int64_t 
         default: out[i] = f_sqrt(a[i]); break;
         }
     }
-    leave_ieee(e);
+    leave_contract(e);
     return ORACLE_OK;
 }
 
@@ -96,7 +97,7 @@ int oracle_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
     if (K > 0) {
         if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N)) return ORACLE_EINVAL;
     }
-    fpenv_t e = enter_ieee();
+    fpenv_t e = enter_contract();
     for (int64_t i = 0; i < M; ++i) {
         for (int64_t j = 0; j < N; ++j) {
             float acc = 0.0f;
@@ -108,7 +109,7 @@ int oracle_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
             C[i * ldc + j] = acc;
         }
     }
-    leave_ieee(e);
+    leave_contract(e);
     return ORACLE_OK;
 }
 
@@ -166,7 +167,8 @@ static float* fold_result(treefold_t* f) {
 }
 
 /* out[i] = Fold(replicas[0][i], ..., replicas[R-1][i]), times fl(1/R) when
- * `average` is set.  max_resident (optional) receives the largest number of
+ * `average` is set.  With one replica the fold performs no operation, so
+ * without the average the output is a copy of the input words.  max_resident (optional) receives the largest number of
  * partial vectors the fold held at once. */
 int oracle_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float* out,
                        int32_t average, int32_t* max_resident) {
@@ -174,18 +176,18 @@ int oracle_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float
     for (int32_t r = 0; r < R; ++r) if (n > 0 && replicas[r] == NULL) return ORACLE_EINVAL;
     if (max_resident) *max_resident = 0;
     if (n == 0) return ORACLE_OK;
-    fpenv_t e = enter_ieee();
+    fpenv_t e = enter_contract();
     treefold_t f;
     f.capacity = 40;
     f.stack = (fold_entry_t*)calloc((size_t)f.capacity, sizeof(fold_entry_t));
     f.depth = 0;
     f.max_depth = 0;
     f.n = n;
-    if (!f.stack) { leave_ieee(e); return ORACLE_ENOMEM; }
+    if (!f.stack) { leave_contract(e); return ORACLE_ENOMEM; }
     for (int32_t r = 0; r < R; ++r) {
         float* part = (float*)malloc((size_t)n * sizeof(float));
-        if (!part) { leave_ieee(e); return ORACLE_ENOMEM; }
-        for (int64_t i = 0; i < n; ++i) part[i] = flush(replicas[r][i]);
+        if (!part) { leave_contract(e); return ORACLE_ENOMEM; }
+        for (int64_t i = 0; i < n; ++i) part[i] = replicas[r][i];
         fold_push(&f, part);
     }
     float* acc = fold_result(&f);
@@ -198,7 +200,7 @@ int oracle_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float
     if (max_resident) *max_resident = f.max_depth;
     free(acc);
     free(f.stack);
-    leave_ieee(e);
+    leave_contract(e);
     return ORACLE_OK;
 }
 
@@ -237,10 +239,10 @@ static adamw_scalars_t adamw_host_scalars(float beta1, float beta2, int64_t step
 
 int oracle_adamw_scalars(float beta1, float beta2, int64_t step, float out4[4]) {
     if (step < 1) return ORACLE_EINVAL;
-    fpenv_t e = enter_ieee();
+    fpenv_t e = enter_contract();
     adamw_scalars_t s = adamw_host_scalars(beta1, beta2, step);
     out4[0] = s.c1; out4[1] = s.c2; out4[2] = s.r1; out4[3] = s.r2;
-    leave_ieee(e);
+    leave_contract(e);
     return ORACLE_OK;
 }
 
@@ -248,7 +250,7 @@ int oracle_adamw(float* state, const float* grad, int64_t n, float lr, float bet
                  float eps, float weight_decay, int64_t step) {
     if (n < 0 || step < 1) return ORACLE_EINVAL;
     if (n == 0) return ORACLE_OK;
-    fpenv_t e = enter_ieee();
+    fpenv_t e = enter_contract();
     const adamw_scalars_t s = adamw_host_scalars(beta1, beta2, step);
     float* W = state;
     float* Mo = state + n;
@@ -275,7 +277,7 @@ int oracle_adamw(float* state, const float* grad, int64_t n, float lr, float bet
         Mo[i] = mn;
         V[i] = vn;
     }
-    leave_ieee(e);
+    leave_contract(e);
     return ORACLE_OK;
 }
 

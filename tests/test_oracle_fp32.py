@@ -1,12 +1,14 @@
 """Pins for the oracle's binary32 contract (CPU only).
 
 OPEN-1B paper, section 2.1 ("Fused multiply-add", "Subnormals") and Table 1:
-one unfused convention, and subnormals flushed to zero everywhere (FTZ zeroes
-a subnormal result, DAZ zeroes a subnormal input).  The reading taken is: do
-the IEEE 754 round-to-nearest-even operation with gradual underflow, then
-replace a subnormal rounded result by a zero of the same sign; a subnormal
-operand reads as a zero of the same sign.  Every expected value here is
-derived by hand from that rule.
+one unfused convention, and subnormals flushed to zero everywhere, with the
+processor path turning on its FTZ mode (a subnormal result becomes zero) and
+DAZ mode (a subnormal input reads as zero).  The reading taken is the x86
+definition of those modes: round to nearest even; a subnormal operand reads
+as a zero of the same sign; a result is replaced by a zero of the same sign
+when it is tiny, i.e. when rounded to 24 significant bits with an unbounded
+exponent it lies below 2^-126.  Every expected value here is derived by hand
+from that rule.
 """
 import numpy as np
 
@@ -52,22 +54,27 @@ def test_subnormal_results_flush_with_sign():
     assert one(OP_DIV, 2.0 ** -125, 2.0) == MIN_NORMAL
 
 
-def test_flush_decision_follows_the_rounded_result():
-    # (1 - 2^-24) * 2^-126 = 2^-126 - 2^-150 exactly.  With gradual underflow
-    # the subnormal spacing is 2^-149, so this is a tie between 0x007FFFFF and
-    # 0x00800000; round-to-even picks 0x00800000 = 2^-126, a normal number,
-    # which is kept.  (A flush decided before rounding would give 0.)
+def test_tininess_is_decided_after_rounding_with_unbounded_exponent():
+    # (1 - 2^-24) * 2^-126 = 2^-126 - 2^-150 = 2^-127 * (2 - 2^-23): exactly 24
+    # significant bits, so rounding with an unbounded exponent leaves it below
+    # 2^-126: tiny, flushed.  (Rounding onto the subnormal grid first would
+    # give the tie 0x007FFFFF / 0x00800000 and keep 2^-126.)
     a = np.uint32(0x3F7FFFFF).view(np.float32)
     assert float(a) == 1.0 - 2.0 ** -24
-    r = one(OP_MUL, a, 2.0 ** -126)
-    assert bits(r) == 0x00800000
-    # (1 - 2^-23) * 2^-126 = 2^-126 - 2^-149 is exactly subnormal: flushed.
+    assert bits(one(OP_MUL, a, 2.0 ** -126)) == 0
+    assert bits(one(OP_MUL, -a, 2.0 ** -126)) == 0x80000000
+    # ((1 - 2^-13) 2^-63) * ((1 + 2^-13) 2^-63) = 2^-126 (1 - 2^-26): rounded
+    # to 24 bits it is 2^-126 itself, so it is not tiny and stays.  (Deciding
+    # on the exact value before rounding would flush it.)
+    x = np.float32((1 - 2.0 ** -13) * 2.0 ** -63)
+    y = np.float32((1 + 2.0 ** -13) * 2.0 ** -63)
+    assert bits(one(OP_MUL, x, y)) == 0x00800000
+    # (1 - 2^-23) * 2^-126 = 2^-126 - 2^-149: exactly subnormal, flushed.
     a2 = np.uint32(0x3F7FFFFE).view(np.float32)
     assert bits(one(OP_MUL, a2, 2.0 ** -126)) == 0
-    # Quotient that rounds up to the smallest normal: (2^-125 - 2^-149) / 2
-    # = 2^-126 - 2^-150, the same tie, so 2^-126.
-    q = np.uint32(0x00FFFFFF).view(np.float32)  # 2^-125 - 2^-149 (normal)
-    assert bits(one(OP_DIV, q, 2.0)) == 0x00800000
+    # Quotient (2^-125 - 2^-149) / 2 = 2^-126 - 2^-150 exactly: tiny, flushed.
+    q = np.uint32(0x00FFFFFF).view(np.float32)
+    assert bits(one(OP_DIV, q, 2.0)) == 0
 
 
 def test_unfused_multiply_then_add():

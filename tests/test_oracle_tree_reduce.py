@@ -173,4 +173,7 @@ def test_r1_and_empty():
     x = np.array([1.5, -2.0, 2.0 ** -130], np.float32)  # last one subnormal: reads as +0
     out = oracle.tree_reduce([x], average=True)
     np.testing.assert_array_equal(out, np.array([1.5, -2.0, 0.0], np.float32))
+    # One replica without the average is no operation at all: the words copy.
+    out = oracle.tree_reduce([x], average=False)
+    assert out.tobytes() == x.tobytes()
     assert oracle.tree_reduce([np.zeros(0, np.float32)] * 3).size == 0
