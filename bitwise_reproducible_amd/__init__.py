@@ -1,0 +1,229 @@
+"""Python binding of librepro.so: bitwise-reproducible training-step ops on MI355X.
+
+Argument marshalling only: every function takes torch tensors on a ROCm
+device, passes their device pointers and the current HIP stream to the C ABI
+of ``include/repro.h`` and returns.  All arithmetic runs in the library's
+HIP kernels; there is no fallback, and a missing library is an error.
+
+Entry points (same names as the C ABI):
+    repro_gemm(A, B, trans_a=False, trans_b=False, out=None)
+    repro_tree_reduce(replicas, out=None, average=True)
+    repro_adamw(state, grad, lr, beta1, beta2, eps, weight_decay, step)
+    repro_state_hash(words, workspace=None) -> 32-byte digest (bytes)
+    repro_state_hash_async(words, digest_out, workspace)
+    repro_fp32_ops(op, a, b, out=None)
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_HERE, "librepro.so")
+_lib = None
+
+REPRO_MAX_REPLICAS = 64
+
+
+class ReproError(RuntimeError):
+    def __init__(self, status: int, what: str):
+        self.status = status
+        super().__init__(f"{what}: {strerror(status)} ({status})")
+
+
+def library():
+    """Load librepro.so (built in-tree by ``__graft_entry__.build()``)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise RuntimeError(f"{LIB_PATH} is missing: build it with `python -c 'import __graft_entry__ as g; "
+                               f"g.build()'` (hipcc for gfx950); there is no fallback path")
+        lib = ctypes.CDLL(LIB_PATH)
+        i32, i64, vp, f32 = ctypes.c_int32, ctypes.c_int64, ctypes.c_void_p, ctypes.c_float
+        lib.repro_spec_version.restype = ctypes.c_char_p
+        lib.repro_spec_version.argtypes = []
+        lib.repro_strerror.restype = ctypes.c_char_p
+        lib.repro_strerror.argtypes = [ctypes.c_int]
+        gemm_args = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.repro_gemm.argtypes = gemm_args + [vp]
+        lib.repro_gemm_variant.argtypes = gemm_args + [i32, vp]
+        lib.repro_tree_reduce.argtypes = [vp, i32, i64, vp, i32, vp]
+        lib.repro_tree_reduce_variant.argtypes = [vp, i32, i64, vp, i32, i32, vp]
+        adamw_args = [vp, vp, i64, f32, f32, f32, f32, f32, i64]
+        lib.repro_adamw.argtypes = adamw_args + [vp]
+        lib.repro_adamw_variant.argtypes = adamw_args + [i32, vp]
+        lib.repro_state_hash_workspace_bytes.restype = i64
+        lib.repro_state_hash_workspace_bytes.argtypes = [i64]
+        lib.repro_state_hash.argtypes = [vp, i64, vp, i64, vp, vp]
+        lib.repro_fp32_ops.argtypes = [i32, vp, vp, vp, i64, vp]
+        for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
+                     "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops"):
+            getattr(lib, name).restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def strerror(status: int) -> str:
+    return library().repro_strerror(int(status)).decode()
+
+
+def spec_version() -> str:
+    return library().repro_spec_version().decode()
+
+
+def _check(status: int, what: str):
+    if status != 0:
+        raise ReproError(status, what)
+
+
+def _stream(stream=None) -> int:
+    import torch
+    s = torch.cuda.current_stream() if stream is None else stream
+    return int(s.cuda_stream)
+
+
+def _f32_device(t, name: str):
+    import torch
+    if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
+        raise TypeError(f"{name} must be a float32 tensor on a ROCm device")
+    return t
+
+
+def _row_major(t, name: str):
+    """(pointer, rows, cols, ld) of a 2-D float32 device tensor with unit column stride."""
+    _f32_device(t, name)
+    if t.dim() != 2:
+        raise ValueError(f"{name} must be 2-D")
+    rows, cols = t.shape
+    if cols > 1 and t.stride(1) != 1:
+        raise ValueError(f"{name} needs unit stride along its last dimension")
+    ld = t.stride(0) if rows > 1 else max(cols, 1)
+    return t.data_ptr(), rows, cols, max(ld, cols, 1)
+
+
+def repro_gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, variant: int = 0, stream=None):
+    """C = op(A) @ op(B), one ascending-k unfused chain per output."""
+    import torch
+    pa, ra, ca, lda = _row_major(A, "A")
+    pb, rb, cb, ldb = _row_major(B, "B")
+    M, K = (ca, ra) if trans_a else (ra, ca)
+    K2, N = (cb, rb) if trans_b else (rb, cb)
+    if K != K2:
+        raise ValueError(f"inner dimensions differ: {K} vs {K2}")
+    if out is None:
+        out = torch.empty((M, N), dtype=torch.float32, device=A.device)
+    pc, rc, cc, ldc = _row_major(out, "out")
+    if (rc, cc) != (M, N):
+        raise ValueError("out has the wrong shape")
+    lib = library()
+    if variant == 0:
+        st = lib.repro_gemm(int(trans_a), int(trans_b), M, N, K, pa, lda, pb, ldb, pc, ldc, _stream(stream))
+    else:
+        st = lib.repro_gemm_variant(int(trans_a), int(trans_b), M, N, K, pa, lda, pb, ldb, pc, ldc, int(variant),
+                                    _stream(stream))
+    _check(st, "repro_gemm")
+    return out
+
+
+def repro_tree_reduce(replicas, out=None, average: bool = True, variant: int = 0, stream=None):
+    """out = TreeFold(replicas) (times fl(1/R) when average)."""
+    import torch
+    reps = list(replicas)
+    R = len(reps)
+    if R < 1 or R > REPRO_MAX_REPLICAS:
+        raise ValueError(f"need 1..{REPRO_MAX_REPLICAS} replicas")
+    n = reps[0].numel()
+    for i, r in enumerate(reps):
+        _f32_device(r, f"replicas[{i}]")
+        if r.numel() != n or not r.is_contiguous():
+            raise ValueError("replicas must be contiguous and of equal size")
+    if out is None:
+        out = torch.empty_like(reps[0])
+    _f32_device(out, "out")
+    if out.numel() != n or not out.is_contiguous():
+        raise ValueError("out must be contiguous with the replicas' size")
+    ptrs = (ctypes.c_void_p * R)(*[r.data_ptr() for r in reps])
+    lib = library()
+    if variant == 0:
+        st = lib.repro_tree_reduce(ctypes.cast(ptrs, ctypes.c_void_p), R, n, out.data_ptr(), int(bool(average)),
+                                   _stream(stream))
+    else:
+        st = lib.repro_tree_reduce_variant(ctypes.cast(ptrs, ctypes.c_void_p), R, n, out.data_ptr(),
+                                           int(bool(average)), int(variant), _stream(stream))
+    _check(st, "repro_tree_reduce")
+    return out
+
+
+def repro_adamw(state, grad, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int,
+                variant: int = 0, stream=None):
+    """In-place AdamW step on the flat state [w | m | v] (3n floats)."""
+    _f32_device(state, "state")
+    _f32_device(grad, "grad")
+    n = grad.numel()
+    if state.numel() != 3 * n or not state.is_contiguous() or not grad.is_contiguous():
+        raise ValueError("state must be a contiguous [w | m | v] of 3 * grad.numel() floats")
+    lib = library()
+    args = (state.data_ptr(), grad.data_ptr(), n, float(lr), float(beta1), float(beta2), float(eps),
+            float(weight_decay), int(step))
+    if variant == 0:
+        st = lib.repro_adamw(*args, _stream(stream))
+    else:
+        st = lib.repro_adamw_variant(*args, int(variant), _stream(stream))
+    _check(st, "repro_adamw")
+    return state
+
+
+def repro_state_hash_workspace_bytes(n_words: int) -> int:
+    v = library().repro_state_hash_workspace_bytes(int(n_words))
+    if v < 0:
+        raise ReproError(int(v), "repro_state_hash_workspace_bytes")
+    return int(v)
+
+
+def hash_workspace(n_words: int, device="cuda"):
+    import torch
+    return torch.empty(repro_state_hash_workspace_bytes(n_words), dtype=torch.uint8, device=device)
+
+
+def repro_state_hash_async(words, digest_out, workspace, stream=None):
+    """Enqueue the state hash; the 32-byte digest lands in ``digest_out`` (device uint8[32])."""
+    import torch
+    _f32_device(words, "words")
+    if not words.is_contiguous():
+        raise ValueError("words must be contiguous")
+    if digest_out.dtype != torch.uint8 or digest_out.numel() < 32 or not digest_out.is_cuda:
+        raise ValueError("digest_out must be a device uint8 tensor of 32 bytes")
+    st = library().repro_state_hash(words.data_ptr(), words.numel(), workspace.data_ptr(), workspace.numel(),
+                                    digest_out.data_ptr(), _stream(stream))
+    _check(st, "repro_state_hash")
+    return digest_out
+
+
+def repro_state_hash(words, workspace=None, stream=None) -> bytes:
+    """32-byte state hash of the words (synchronises with the stream to return it)."""
+    import torch
+    if workspace is None:
+        workspace = hash_workspace(words.numel(), words.device)
+    digest = torch.empty(32, dtype=torch.uint8, device=words.device)
+    repro_state_hash_async(words, digest, workspace, stream)
+    return bytes(digest.cpu().numpy().tobytes())
+
+
+def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
+    """One contract operation per element (diagnostic; see repro.h)."""
+    import torch
+    _f32_device(a, "a")
+    b = a if b is None else b
+    _f32_device(b, "b")
+    if out is None:
+        out = torch.empty_like(a)
+    if not (a.is_contiguous() and b.is_contiguous() and out.is_contiguous()) or a.numel() != b.numel():
+        raise ValueError("a, b, out must be contiguous and of equal size")
+    _check(library().repro_fp32_ops(int(op), a.data_ptr(), b.data_ptr(), out.data_ptr(), a.numel(),
+                                    _stream(stream)), "repro_fp32_ops")
+    return out
+
+
+__all__ = ["repro_gemm", "repro_tree_reduce", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
+           "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
+           "ReproError", "LIB_PATH"]

@@ -1,0 +1,169 @@
+// C-ABI front end of librepro.so: argument checks, the host-side scalars,
+// and the kernel launches.  See include/repro.h for the contract of every
+// entry point.
+#include <hip/hip_runtime.h>
+#include <math.h>
+#include <stdint.h>
+#include <xmmintrin.h>
+
+#include "internal.h"
+#include "repro.h"
+
+namespace {
+
+using repro::AdamwScalars;
+using repro::ReplicaPtrs;
+
+bool aligned4(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 3u) == 0; }
+
+int status_of(hipError_t e) { return e == hipSuccess ? REPRO_OK : REPRO_EDEVICE; }
+
+// Host binary32 arithmetic under the contract of repro.h: the SSE control
+// register is set to round-to-nearest with FTZ and DAZ on for the duration
+// (the x86 definition of the flush rule), and restored afterwards.
+class HostFp32 {
+ public:
+  HostFp32() : saved_(_mm_getcsr()) { _mm_setcsr((saved_ & ~0x6000u) | 0x8000u | 0x0040u | 0x1F80u); }
+  ~HostFp32() { _mm_setcsr(saved_); }
+  static float sub(float a, float b) { return a - b; }
+  static float mul(float a, float b) { return a * b; }
+  static float div(float a, float b) { return a / b; }
+
+ private:
+  unsigned saved_;
+};
+
+// Appendix A.3 reciprocal: fl(1 / R) on the host.
+float replica_reciprocal(int R) {
+  HostFp32 env;
+  return HostFp32::div(1.0f, (float)R);
+}
+
+// AdamW host scalars: c = 1 - beta, beta^step as step-1 serial products, and
+// the reciprocals of the bias corrections.
+AdamwScalars adamw_scalars(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
+  HostFp32 env;
+  AdamwScalars s;
+  s.lr = lr;
+  s.beta1 = beta1;
+  s.beta2 = beta2;
+  s.eps = eps;
+  s.wd = wd;
+  s.c1 = HostFp32::sub(1.0f, s.beta1);
+  s.c2 = HostFp32::sub(1.0f, s.beta2);
+  float pow1 = s.beta1, pow2 = s.beta2;
+  for (int64_t t = 2; t <= step; ++t) {
+    pow1 = HostFp32::mul(pow1, s.beta1);
+    pow2 = HostFp32::mul(pow2, s.beta2);
+  }
+  s.r1 = HostFp32::div(1.0f, HostFp32::sub(1.0f, pow1));
+  s.r2 = HostFp32::div(1.0f, HostFp32::sub(1.0f, pow2));
+  return s;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char* repro_spec_version(void) { return "repro-spec-1"; }
+
+const char* repro_strerror(int status) {
+  switch (status) {
+    case REPRO_OK: return "ok";
+    case REPRO_EINVAL: return "invalid argument";
+    case REPRO_EALIGN: return "device pointer not 4-byte aligned";
+    case REPRO_EDEVICE: return "HIP launch or runtime error";
+    case REPRO_ESPACE: return "workspace too small";
+    default: return "unknown status";
+  }
+}
+
+int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > 2) return REPRO_EINVAL;
+  if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return REPRO_EINVAL;
+  if (M == 0 || N == 0) return REPRO_OK;
+  if (C == nullptr || ldc < N) return REPRO_EINVAL;
+  if (K > 0) {
+    if (A == nullptr || B == nullptr) return REPRO_EINVAL;
+    if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N)) return REPRO_EINVAL;
+    if (!aligned4(A) || !aligned4(B)) return REPRO_EALIGN;
+  }
+  if (!aligned4(C)) return REPRO_EALIGN;
+  return status_of(repro::launch_gemm(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, variant,
+                                      static_cast<hipStream_t>(stream)));
+}
+
+int repro_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+               const float* B, int64_t ldb, float* C, int64_t ldc, void* stream) {
+  return repro_gemm_variant(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, 0, stream);
+}
+
+int repro_tree_reduce_variant(const float* const* replicas, int32_t R, int64_t n, float* out, int32_t average,
+                              int32_t variant, void* stream) {
+  if (replicas == nullptr || R < 1 || R > REPRO_MAX_REPLICAS || n < 0 || variant < 0 || variant > 2)
+    return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (out == nullptr) return REPRO_EINVAL;
+  ReplicaPtrs reps = {};
+  for (int r = 0; r < R; ++r) {
+    if (replicas[r] == nullptr) return REPRO_EINVAL;
+    if (!aligned4(replicas[r])) return REPRO_EALIGN;
+    reps.p[r] = replicas[r];
+  }
+  if (!aligned4(out)) return REPRO_EALIGN;
+  const float rR = replica_reciprocal(R);
+  return status_of(repro::launch_tree_reduce(reps, R, n, out, average != 0, rR, variant,
+                                             static_cast<hipStream_t>(stream)));
+}
+
+int repro_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float* out, int32_t average,
+                      void* stream) {
+  return repro_tree_reduce_variant(replicas, R, n, out, average, 0, stream);
+}
+
+int repro_adamw_variant(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
+                        float weight_decay, int64_t step, int32_t variant, void* stream) {
+  if (n < 0 || step < 1 || variant < 0 || variant > 1) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (state == nullptr || grad == nullptr) return REPRO_EINVAL;
+  if (!aligned4(state) || !aligned4(grad)) return REPRO_EALIGN;
+  const AdamwScalars s = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step);
+  return status_of(repro::launch_adamw(state, grad, n, s, variant, static_cast<hipStream_t>(stream)));
+}
+
+int repro_adamw(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
+                float weight_decay, int64_t step, void* stream) {
+  return repro_adamw_variant(state, grad, n, lr, beta1, beta2, eps, weight_decay, step, 0, stream);
+}
+
+int64_t repro_state_hash_workspace_bytes(int64_t n_words) {
+  if (n_words < 0) return REPRO_EINVAL;
+  repro::HashPlan plan;
+  repro::plan_state_hash(n_words, &plan);
+  return plan.total_bytes;
+}
+
+int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
+                     void* stream) {
+  if (n_words < 0 || workspace == nullptr || digest_out == nullptr) return REPRO_EINVAL;
+  if (n_words > 0 && words == nullptr) return REPRO_EINVAL;
+  if (n_words > 0 && !aligned4(words)) return REPRO_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 || (reinterpret_cast<uintptr_t>(digest_out) & 15u) != 0)
+    return REPRO_EALIGN;
+  repro::HashPlan plan;
+  repro::plan_state_hash(n_words, &plan);
+  if (ws_bytes < plan.total_bytes) return REPRO_ESPACE;
+  return status_of(repro::launch_state_hash(words, n_words, static_cast<uint8_t*>(workspace), plan, digest_out,
+                                            static_cast<hipStream_t>(stream)));
+}
+
+int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream) {
+  if (op < 0 || op > 4 || n < 0) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (a == nullptr || b == nullptr || out == nullptr) return REPRO_EINVAL;
+  if (!aligned4(a) || !aligned4(b) || !aligned4(out)) return REPRO_EALIGN;
+  return status_of(repro::launch_fp32_ops(op, a, b, out, n, static_cast<hipStream_t>(stream)));
+}
+
+}  // extern "C"

@@ -1,0 +1,258 @@
+// repro_gemm: C = op(A) * op(B) with one ascending-k chain per output.
+//
+// "OPEN-1B: A Fully Auditable Training Run", section 2.1 ("Reduction order":
+// every sum inside a matrix multiply in one fixed order; "Fused
+// multiply-add": explicitly unfused multiply and add on the GPU) and section
+// 6, item 1.  The declared order: acc = +0, then for k = 0, 1, ..., K-1,
+// acc = fl(acc + fl(a_ik * b_kj)).
+//
+// Design for gfx950:
+//  - gfx950 has no unfused multiply-add instruction, and fused ones round
+//    once, so every step is a v_mul_f32 followed by a v_add_f32.  The file
+//    is built with -ffp-contract=off and without packed-fp32 instructions;
+//    the instruction-mix audit in the tests checks that no v_fma / v_fmac /
+//    v_pk_* appears in the kernels.
+//  - It is built with -fgpu-flush-denormals-to-zero: the kernel descriptor
+//    sets the fp32 denormal mode to "flush inputs and outputs", so the VALU
+//    itself applies the subnormal rule of section 2.1 at no cost (on gfx950
+//    this flush is the x86 FTZ/DAZ rule bit for bit; repro_fp32_ops exposes
+//    the same v_mul_f32 / v_add_f32 for the directed boundary tests).
+//  - Work is split over output tiles only.  A workgroup of 256 lanes owns a
+//    BM x BN tile; each lane owns a TM x TN register tile and walks the
+//    K dimension in ascending BK-wide slabs staged through LDS (double
+//    buffered, one barrier per slab), so every output keeps a single serial
+//    chain in its own register.  No split-k, no atomics, no cross-lane sums.
+//  - A and B slabs are loaded with 16-byte global loads when the layout
+//    allows and transposed into k-major LDS rows, so that the inner loop
+//    reads a and b fragments as 16-byte LDS vectors.
+#include <hip/hip_runtime.h>
+
+#include "internal.h"
+
+namespace repro {
+namespace {
+
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+struct GemmTile {
+  static constexpr int TX = BN / TN;  // lanes along n
+  static constexpr int TY = BM / TM;  // lanes along m
+  static constexpr int NT = TX * TY;  // lanes per workgroup
+  static constexpr int PAD = 4;       // keeps 16-byte alignment of LDS rows
+  static constexpr int LA = BM * BK / 4 / NT;  // 4-element chunks of A per lane per slab
+  static constexpr int LB = BK * BN / 4 / NT;
+  static_assert(TM % 4 == 0 && TN % 4 == 0, "register tiles are read as 16-byte vectors");
+  static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
+  static_assert(BK % 4 == 0, "BK must be a multiple of 4");
+};
+
+// Loads one slab chunk (4 consecutive elements along the contiguous
+// dimension of the stored matrix) with bounds checks; out-of-range elements
+// read as zero and are never used by an in-range output.
+template <bool VEC>
+__device__ __forceinline__ float4 load_chunk(const float* __restrict__ p, int64_t row, int64_t col, int64_t ld,
+                                             int64_t rows, int64_t cols) {
+  float4 v = make_float4(0.f, 0.f, 0.f, 0.f);
+  if (row < rows) {
+    const float* q = p + row * ld + col;
+    if constexpr (VEC) {
+      if (col < cols) v = *reinterpret_cast<const float4*>(q);
+    } else {
+      if (col + 0 < cols) v.x = q[0];
+      if (col + 1 < cols) v.y = q[1];
+      if (col + 2 < cols) v.z = q[2];
+      if (col + 3 < cols) v.w = q[3];
+    }
+  }
+  return v;
+}
+
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
+  using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
+  __shared__ __attribute__((aligned(16))) float As[2][BK][BM + T::PAD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + T::PAD];
+
+  const int tile = blockIdx.x;
+  const int64_t i0 = (int64_t)(tile / tiles_n) * BM;
+  const int64_t j0 = (int64_t)(tile % tiles_n) * BN;
+  const int tid = threadIdx.x;
+  const int tx = tid % T::TX;
+  const int ty = tid / T::TX;
+
+  float4 ra[T::LA], rb[T::LB];
+
+  // Global -> registers for the slab starting at k0.
+  auto load_slab = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < T::LA; ++q) {
+      const int f = tid + q * T::NT;
+      if constexpr (!TA) {  // A is M x K row-major: rows i, contiguous k
+        const int r = f / (BK / 4), c4 = f % (BK / 4);
+        ra[q] = load_chunk<VEC>(A, i0 + r, k0 + 4 * c4, lda, M, K);
+      } else {  // A stored K x M: rows k, contiguous i
+        const int c = f / (BM / 4), r4 = f % (BM / 4);
+        ra[q] = load_chunk<VEC>(A, k0 + c, i0 + 4 * r4, lda, K, M);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < T::LB; ++q) {
+      const int f = tid + q * T::NT;
+      if constexpr (!TB) {  // B is K x N row-major: rows k, contiguous j
+        const int c = f / (BN / 4), j4 = f % (BN / 4);
+        rb[q] = load_chunk<VEC>(B, k0 + c, j0 + 4 * j4, ldb, K, N);
+      } else {  // B stored N x K: rows j, contiguous k
+        const int j = f / (BK / 4), c4 = f % (BK / 4);
+        rb[q] = load_chunk<VEC>(B, j0 + j, k0 + 4 * c4, ldb, N, K);
+      }
+    }
+  };
+
+  // Registers -> LDS, k-major.
+  auto store_slab = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < T::LA; ++q) {
+      const int f = tid + q * T::NT;
+      if constexpr (!TA) {
+        const int r = f / (BK / 4), c4 = f % (BK / 4);
+        As[buf][4 * c4 + 0][r] = ra[q].x;
+        As[buf][4 * c4 + 1][r] = ra[q].y;
+        As[buf][4 * c4 + 2][r] = ra[q].z;
+        As[buf][4 * c4 + 3][r] = ra[q].w;
+      } else {
+        const int c = f / (BM / 4), r4 = f % (BM / 4);
+        *reinterpret_cast<float4*>(&As[buf][c][4 * r4]) = ra[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < T::LB; ++q) {
+      const int f = tid + q * T::NT;
+      if constexpr (!TB) {
+        const int c = f / (BN / 4), j4 = f % (BN / 4);
+        *reinterpret_cast<float4*>(&Bs[buf][c][4 * j4]) = rb[q];
+      } else {
+        const int j = f / (BK / 4), c4 = f % (BK / 4);
+        Bs[buf][4 * c4 + 0][j] = rb[q].x;
+        Bs[buf][4 * c4 + 1][j] = rb[q].y;
+        Bs[buf][4 * c4 + 2][j] = rb[q].z;
+        Bs[buf][4 * c4 + 3][j] = rb[q].w;
+      }
+    }
+  };
+
+  float acc[TM][TN];
+#pragma unroll
+  for (int i = 0; i < TM; ++i)
+#pragma unroll
+    for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;  // the chain starts at +0
+
+  // One k step: every output of the lane takes fl(acc + fl(a * b)).
+  auto mac_step = [&](int buf, int kk) {
+    float a[TM], b[TN];
+#pragma unroll
+    for (int g = 0; g < TM / 4; ++g)
+      *reinterpret_cast<float4*>(&a[4 * g]) =
+          *reinterpret_cast<const float4*>(&As[buf][kk][g * 4 * T::TY + ty * 4]);
+#pragma unroll
+    for (int g = 0; g < TN / 4; ++g)
+      *reinterpret_cast<float4*>(&b[4 * g]) =
+          *reinterpret_cast<const float4*>(&Bs[buf][kk][g * 4 * T::TX + tx * 4]);
+#pragma unroll
+    for (int i = 0; i < TM; ++i)
+#pragma unroll
+      for (int j = 0; j < TN; ++j) {
+        const float p = a[i] * b[j];
+        acc[i][j] = acc[i][j] + p;
+      }
+  };
+
+  const int64_t nslabs = (K + BK - 1) / BK;
+  if (nslabs > 0) {
+    load_slab(0);
+    store_slab(0);
+    __syncthreads();
+    for (int64_t s = 0; s < nslabs; ++s) {
+      const int buf = (int)(s & 1);
+      if (s + 1 < nslabs) load_slab((s + 1) * BK);
+      const int64_t kleft = K - s * BK;
+      if (kleft >= BK) {
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
+      } else {
+        for (int kk = 0; kk < (int)kleft; ++kk) mac_step(buf, kk);
+      }
+      if (s + 1 < nslabs) store_slab(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Epilogue: lane rows g*4*TY + ty*4 + e, columns h*4*TX + tx*4 + 0..3.
+  const bool vec_c = VEC && (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
+#pragma unroll
+  for (int g = 0; g < TM / 4; ++g)
+#pragma unroll
+    for (int e = 0; e < 4; ++e) {
+      const int64_t row = i0 + g * 4 * T::TY + ty * 4 + e;
+      if (row >= M) continue;
+#pragma unroll
+      for (int h = 0; h < TN / 4; ++h) {
+        const int64_t col = j0 + h * 4 * T::TX + tx * 4;
+        float* out = C + row * ldc + col;
+        const float* v = &acc[g * 4 + e][h * 4];
+        if (vec_c && col + 3 < N) {
+          *reinterpret_cast<float4*>(out) = make_float4(v[0], v[1], v[2], v[3]);
+        } else {
+#pragma unroll
+          for (int t = 0; t < 4; ++t)
+            if (col + t < N) out[t] = v[t];
+        }
+      }
+    }
+}
+
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
+                        int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
+  using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
+  const int64_t tiles_m = (M + BM - 1) / BM;
+  const int64_t tiles_n = (N + BN - 1) / BN;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
+                     M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
+  return hipGetLastError();
+}
+
+template <int BM, int BN, int BK, int TM, int TN>
+hipError_t dispatch(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                    const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
+#define REPRO_GEMM_CASE(TA_, TB_)                                                                          \
+  if (ta == TA_ && tb == TB_)                                                                              \
+    return vec ? launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, true>(M, N, K, A, lda, B, ldb, C, ldc, stream) \
+               : launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, false>(M, N, K, A, lda, B, ldb, C, ldc, stream);
+  REPRO_GEMM_CASE(0, 0)
+  REPRO_GEMM_CASE(1, 0)
+  REPRO_GEMM_CASE(0, 1)
+  REPRO_GEMM_CASE(1, 1)
+#undef REPRO_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
+}  // namespace
+
+hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, hipStream_t stream) {
+  auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
+  // 16-byte loads need aligned bases, leading dimensions that keep rows
+  // aligned, and a contiguous extent that is a multiple of 4 so that a
+  // chunk is either wholly inside or wholly outside the matrix.
+  const int64_t a_contig = trans_a ? M : K;
+  const int64_t b_contig = trans_b ? K : N;
+  const bool vec = variant != 1 && al16(A) && al16(B) && lda % 4 == 0 && ldb % 4 == 0 && a_contig % 4 == 0 &&
+                   b_contig % 4 == 0;
+  if (variant == 2) return dispatch<64, 64, 16, 4, 4>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return dispatch<128, 128, 16, 8, 8>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+}
+
+}  // namespace repro

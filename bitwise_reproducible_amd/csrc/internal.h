@@ -1,0 +1,46 @@
+// Internal interface between the C-ABI front end (api.cpp) and the kernel
+// translation units.  Every launcher enqueues on `stream` and returns the
+// hipError_t of the launch; argument checking is done by the front end.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "repro.h"
+
+namespace repro {
+
+struct ReplicaPtrs {
+  const float* p[REPRO_MAX_REPLICAS];
+};
+
+// Host-prepared AdamW scalars (binary32, computed under the contract).
+struct AdamwScalars {
+  float lr, beta1, beta2, eps, wd;
+  float c1, c2, r1, r2;
+};
+
+// elementwise.hip
+hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* out, int average, float rR,
+                              int variant, hipStream_t stream);
+hipError_t launch_adamw(float* state, const float* grad, int64_t n, const AdamwScalars& s, int variant,
+                        hipStream_t stream);
+hipError_t launch_fp32_ops(int op, const float* a, const float* b, float* out, int64_t n, hipStream_t stream);
+
+// gemm.hip
+hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, hipStream_t stream);
+
+// state_hash.hip
+struct HashPlan {
+  static constexpr int kMaxLevels = 64;
+  int levels;                       // number of levels, leaves included
+  int64_t count[kMaxLevels];        // nodes per level
+  int64_t offset[kMaxLevels];       // byte offset of each level's digests in the workspace
+  int64_t total_bytes;              // workspace bytes needed
+};
+void plan_state_hash(int64_t n_words, HashPlan* plan);
+hipError_t launch_state_hash(const float* words, int64_t n_words, uint8_t* workspace, const HashPlan& plan,
+                             uint8_t* digest_out, hipStream_t stream);
+
+}  // namespace repro

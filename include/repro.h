@@ -14,10 +14,13 @@
  *   - Appendix B and Figure 11 (a BLAKE2b state hash per step).
  *
  * Numeric contract shared by every call: IEEE 754 binary32, round to
- * nearest even, no fused multiply-add.  A subnormal operand reads as a zero
- * of the same sign.  A result whose IEEE (gradual-underflow) rounding is
- * subnormal becomes a zero of the same sign.  Division and square root are
- * correctly rounded.  Inputs are assumed finite.
+ * nearest even, no fused multiply-add.  Subnormals are flushed the way the
+ * processor path's FTZ and DAZ modes do it (section 2.1 "Subnormals"), with
+ * the x86 definition of those modes: a subnormal operand reads as a zero of
+ * the same sign, and a result that is tiny - below 2^-126 once rounded to 24
+ * significant bits with an unbounded exponent - becomes a zero of the same
+ * sign.  Division and square root are correctly rounded.  Inputs are assumed
+ * finite.
  *
  * Determinism promise: output bits depend only on the input bits and the
  * arguments, never on the stream, the launch configuration (the *_variant
@@ -175,12 +178,10 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
                      uint8_t* digest_out, void* stream);
 
 /*
- * repro_fp32_ops: one contract operation per element, with the same device
- * arithmetic the kernels use (diagnostic entry point for directed tests of
- * the flush rule, division and square root).
- *   op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (b ignored): the element-wise
- *        arithmetic of repro_tree_reduce and repro_adamw;
- *   op 5 mul, 6 add: the arithmetic of repro_gemm's multiply-accumulate.
+ * repro_fp32_ops: one contract operation per element, out[i] = a[i] op b[i],
+ * in the same device arithmetic the kernels use (a diagnostic entry point for
+ * directed tests of the flush rule, division and square root).
+ *   op 0 add, 1 sub, 2 mul, 3 div, 4 sqrt (of a; b is read but ignored).
  * a, b, out: device pointers to n floats.
  */
 int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream);

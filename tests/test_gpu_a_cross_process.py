@@ -1,0 +1,58 @@
+"""Bits do not depend on the process: two fresh processes, ten runs each.
+
+OPEN-1B paper, section 2 (bitwise reproducibility, not mere run-to-run
+determinism); the lab note on cross-process reproducibility traces drift to
+reduction orders chosen at run time, which this library never does.
+
+This module is named to run before the other GPU tests: the test process
+itself never touches the GPU here; it only starts two child processes and
+compares what they print, and checks one run against the oracle.
+"""
+import hashlib
+import json
+import os
+import subprocess
+import sys
+
+import numpy as np
+import pytest
+
+import oracle
+import synth
+
+pytestmark = pytest.mark.gpu
+
+CHILD = os.path.join(os.path.dirname(os.path.abspath(__file__)), "cross_process_child.py")
+
+
+def _run_child():
+    res = subprocess.run([sys.executable, CHILD], capture_output=True, text=True, timeout=300)
+    assert res.returncode == 0, res.stderr[-2000:]
+    return json.loads(res.stdout.strip().splitlines()[-1])
+
+
+def _sha(x) -> str:
+    return hashlib.sha256(np.ascontiguousarray(x, np.float32).tobytes()).hexdigest()
+
+
+def test_two_processes_ten_runs_each_agree_with_the_oracle():
+    first = _run_child()
+    second = _run_child()
+    assert first["pid"] != second["pid"]
+    runs = first["runs"] + second["runs"]
+    for r in runs[1:]:
+        assert r == runs[0]
+    # ...and the bits are the oracle's.
+    cfg = synth.TINY
+    a, b = synth.tiny_gemm_inputs()
+    reps = [synth.tiny_replica(r) for r in range(cfg["R"])]
+    g = oracle.tree_reduce(reps)
+    n = cfg["n"]
+    state = np.concatenate([synth.tiny_adamw_weights(n), np.zeros(2 * n, np.float32)])
+    st = oracle.adamw(state, g, cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"], cfg["wd"], cfg["step"])
+    assert runs[0]["gemm"] == _sha(oracle.gemm(a, b))
+    assert runs[0]["reduce"] == _sha(g)
+    assert runs[0]["adamw"] == _sha(st)
+    assert runs[0]["state_hash"] == oracle.state_hash(st).hex()
+    big = [synth.reduce_replica(r) for r in range(synth.REDUCE["R"])]
+    assert runs[0]["reduce_workload"] == _sha(oracle.tree_reduce(big))
