@@ -1,0 +1,332 @@
+#!/usr/bin/env python
+"""Benchmark of the reproducible training-step operations on one MI355X.
+
+One step is one pass of the whole hot path over the full synthetic workloads,
+every input already resident in HBM:
+  1. repro_tree_reduce   R = 8 replicas x 16,777,216 floats, x fl(1/8)
+  2. repro_gemm          Y[8192x8192] = X[8192x2048] W[2048x8192]
+  3. repro_adamw         flat [w|m|v] of n = 1.2e9, grad n (step counter advances)
+  4. repro_state_hash    BLAKE2b tree over the 14.4 GB [w|m|v]
+  5. repro_gemm          dW[2048x8192] = X^T dY, X[16384x2048], dY[16384x8192]
+Each op is bracketed by HIP events on the stream it runs on.  `value` is the
+GB/s of the memory-side ops (1, 3, 4: algorithmic bytes over their summed
+event time); the GEMMs are reported in GFLOP/s beside it.  After the timed
+steps the outputs are checked against the CPU oracle (every word of the
+reduce output, sampled rows and columns of both GEMMs, sampled AdamW
+elements replayed through every step, sampled hash leaves), and the oracle
+itself is timed on a bounded sample as the CPU baseline.
+
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+"""
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "bit-exact GB/s (reduce+AdamW+hash) and GFLOP/s (repro_gemm) vs roofline, 1 GPU"
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
+FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
+# VALU issue rate: 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T
+# lane-operations/s (the vendor fp32 figure is this rate times 2 flops per
+# FMA).  The declared MAC is a multiply and an add, two lane-ops for two
+# flops, so the GEMM's ceiling is 78.6 TFLOP/s.  32-bit integer ops issue at
+# the same rate (measured), which bounds the hash.
+VALU_LANE_OPS = 256 * 128 * 2.4e9
+GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
+# BLAKE2b: per 128-byte block 12 rounds x 8 G; a G is 6 64-bit adds (2
+# lane-ops each), 4 64-bit xors (2 each) and 3 rotations by 24/16/63 (2 each;
+# the rotation by 32 is a register swap): 26 lane-ops, plus 16 xors for the
+# feed-forward: 2512 lane-ops per 128 bytes.
+HASH_OPS_PER_BYTE = (12 * 8 * 26 + 16) / 128
+HASH_PEAK_GBS = VALU_LANE_OPS / HASH_OPS_PER_BYTE / 1e9
+
+
+def log(*a):
+    print("[bench]", *a, file=sys.stderr, flush=True)
+
+
+def parse():
+    p = argparse.ArgumentParser()
+    p.add_argument("--gpus", type=int, default=1)
+    p.add_argument("--steps", type=int, default=10)
+    p.add_argument("--warmup", type=int, default=3)
+    p.add_argument("--no-verify", action="store_true", help="skip the oracle check after timing")
+    p.add_argument("--no-cpu-baseline", action="store_true")
+    return p.parse_args()
+
+
+class Upload:
+    """Generate a synthetic tensor chunk by chunk into pinned host memory and
+    copy each chunk to its device slice, optionally keeping sampled values."""
+
+    def __init__(self, torch, chunk=1 << 26):
+        self.torch = torch
+        self.buf = torch.empty(chunk, dtype=torch.float32, pin_memory=True)
+        self.chunk = chunk
+
+    def fill(self, dst, gen, n, sample_idx=None):
+        import numpy as np
+        keep = None if sample_idx is None else np.empty(sample_idx.size, np.float32)
+        host = self.buf.numpy()
+        for off in range(0, n, self.chunk):
+            m = min(self.chunk, n - off)
+            gen(m, offset=off, out=host[:m])
+            dst[off:off + m].copy_(self.buf[:m], non_blocking=False)
+            if keep is not None:
+                lo, hi = np.searchsorted(sample_idx, [off, off + m])
+                keep[lo:hi] = host[sample_idx[lo:hi] - off]
+        return keep
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "The operations shard by contiguous element ranges or output tiles with no change of bits; "
+              "the design is described in DESIGN.md.", file=sys.stderr)
+        sys.exit(2)
+    import numpy as np
+    import torch
+
+    import bitwise_reproducible_amd as br
+    import synth
+
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    up = Upload(torch)
+    t_setup = time.time()
+
+    # 1. Gradient reduction workload.
+    RC = synth.REDUCE
+    reps = []
+    for r in range(RC["R"]):
+        d = torch.empty(RC["n"], dtype=torch.float32, device=dev)
+        up.fill(d, lambda m, offset, out, r=r: synth.reduce_replica(r, m, offset=offset, out=out), RC["n"])
+        reps.append(d)
+    g_red = torch.empty(RC["n"], dtype=torch.float32, device=dev)
+    # 2. Forward GEMM workload.
+    GC = synth.GEMM
+    X3 = torch.empty(GC["M"] * GC["K"], dtype=torch.float32, device=dev)
+    W3 = torch.empty(GC["K"] * GC["N"], dtype=torch.float32, device=dev)
+    up.fill(X3, lambda m, offset, out: synth.generate(m, synth.NORMAL, synth.tid(3, 0), 1.0, offset=offset, out=out),
+            X3.numel())
+    up.fill(W3, lambda m, offset, out: synth.generate(m, synth.NORMAL, synth.tid(3, 1), 0.02, offset=offset,
+                                                      out=out), W3.numel())
+    X3 = X3.view(GC["M"], GC["K"])
+    W3 = W3.view(GC["K"], GC["N"])
+    Y3 = torch.empty(GC["M"], GC["N"], dtype=torch.float32, device=dev)
+    # 3-4. Optimizer + hash workload.
+    AC = synth.ADAMW
+    n = AC["n"]
+    rng = np.random.default_rng(12)
+    aidx = np.unique(np.concatenate([np.arange(0, 1024), np.arange(n - 1024, n), rng.integers(0, n, 60_000)]))
+    state = torch.empty(3 * n, dtype=torch.float32, device=dev)
+    grad = torch.empty(n, dtype=torch.float32, device=dev)
+    log(f"generating the optimizer state, 3 x {n} + {n} floats")
+    s_w = up.fill(state[:n], lambda m, offset, out: synth.adamw_w(m, offset=offset, out=out), n, aidx)
+    s_m = up.fill(state[n:2 * n], lambda m, offset, out: synth.adamw_m(m, offset=offset, out=out), n, aidx)
+    s_v = up.fill(state[2 * n:], lambda m, offset, out: synth.adamw_v(m, offset=offset, out=out), n, aidx)
+    s_g = up.fill(grad, lambda m, offset, out: synth.adamw_g(m, offset=offset, out=out), n, aidx)
+    ws = br.hash_workspace(3 * n, dev)
+    digest = torch.empty(32, dtype=torch.uint8, device=dev)
+    # 5. Weight-gradient workload.
+    DC = synth.DW
+    X5 = torch.empty(DC["K"] * DC["M"], dtype=torch.float32, device=dev)
+    dY5 = torch.empty(DC["K"] * DC["N"], dtype=torch.float32, device=dev)
+    up.fill(X5, lambda m, offset, out: synth.generate(m, synth.STUDENT_T3, synth.tid(5, 0), 1e-2, offset=offset,
+                                                      out=out), X5.numel())
+    up.fill(dY5, lambda m, offset, out: synth.generate(m, synth.STUDENT_T3, synth.tid(5, 1), 1e-2, offset=offset,
+                                                       out=out), dY5.numel())
+    X5 = X5.view(DC["K"], DC["M"])
+    dY5 = dY5.view(DC["K"], DC["N"])
+    dW5 = torch.empty(DC["M"], DC["N"], dtype=torch.float32, device=dev)
+    torch.cuda.synchronize()
+    del up
+    log(f"inputs resident in HBM after {time.time() - t_setup:.1f} s")
+
+    hp = dict(lr=AC["lr"], beta1=AC["beta1"], beta2=AC["beta2"], eps=AC["eps"], weight_decay=AC["wd"])
+    ops = ["tree_reduce", "gemm_fwd", "adamw", "state_hash", "gemm_dw"]
+    step_counter = [AC["step"]]
+
+    def one_step(events=None):
+        rec = (lambda i: events[i].record()) if events else (lambda i: None)
+        rec(0)
+        br.repro_tree_reduce(reps, out=g_red)
+        rec(1)
+        br.repro_gemm(X3, W3, out=Y3)
+        rec(2)
+        br.repro_adamw(state, grad, step=step_counter[0], **hp)
+        step_counter[0] += 1
+        rec(3)
+        br.repro_state_hash_async(state, digest, ws)
+        rec(4)
+        br.repro_gemm(X5, dY5, trans_a=True, out=dW5)
+        rec(5)
+
+    for _ in range(args.warmup):
+        one_step()
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for s in range(args.steps):
+        one_step(evs[s])
+    torch.cuda.synchronize()
+    t1 = time.perf_counter()
+    ms_per_step = (t1 - t0) * 1e3 / args.steps
+    op_ms = {op: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
+             for i, op in enumerate(ops)}
+
+    # Algorithmic work per launch.
+    bytes_reduce = (RC["R"] + 1) * 4 * RC["n"]
+    bytes_adamw = 28 * n
+    bytes_hash = 12 * n
+    flops_fwd = 2 * GC["M"] * GC["N"] * GC["K"]
+    flops_dw = 2 * DC["M"] * DC["N"] * DC["K"]
+    mem_ms = op_ms["tree_reduce"] + op_ms["adamw"] + op_ms["state_hash"]
+    value = (bytes_reduce + bytes_adamw + bytes_hash) / (mem_ms * 1e-3) / 1e9
+    gemm_ms = op_ms["gemm_fwd"] + op_ms["gemm_dw"]
+    gemm_gflops = (flops_fwd + flops_dw) / (gemm_ms * 1e-3) / 1e9
+
+    def roof(op):
+        ms = op_ms[op]
+        if op in ("gemm_fwd", "gemm_dw"):
+            f = flops_fwd if op == "gemm_fwd" else flops_dw
+            ach = f / (ms * 1e-3) / 1e12
+            return {"bound": "alu", "achieved": round(ach, 3), "peak": round(GEMM_PEAK_TFLOPS, 2),
+                    "unit": "TFLOP/s", "frac": round(ach / GEMM_PEAK_TFLOPS, 4), "traffic": None,
+                    "frac_of_fp32_vector_peak": round(ach / FP32_VECTOR_PEAK, 4)}
+        b = {"tree_reduce": bytes_reduce, "adamw": bytes_adamw, "state_hash": bytes_hash}[op]
+        ach = b / (ms * 1e-3) / 1e9
+        if op == "state_hash":  # integer-VALU bound: ~19.6 lane-ops per byte
+            return {"bound": "alu", "achieved": round(ach, 1), "peak": round(HASH_PEAK_GBS, 1), "unit": "GB/s",
+                    "frac": round(ach / HASH_PEAK_GBS, 4), "traffic": None,
+                    "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4)}
+        return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+
+    per_op = {op: {"ms": round(op_ms[op], 4), **roof(op)} for op in ops}
+    dominant = max(ops, key=lambda o: op_ms[o])
+    out = {
+        "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
+        "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded Philox4x64-10, recipes in DESIGN.md)",
+        "config": {"workload": "reduce R=8 n=16777216; gemm 8192x2048 @ 2048x8192; adamw+state_hash n=1.2e9 "
+                               "[w|m|v] 14.4 GB; dW 2048x8192 K=16384",
+                   "parallelism": "none (1 GPU)"},
+        "gemm": {"value": round(gemm_gflops, 1), "unit": "GFLOP/s"},
+        "ops": per_op,
+        "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if k != "ms"}},
+    }
+
+    if not args.no_verify:
+        out["verified"] = verify(torch, np, br, reps, g_red, X3, W3, Y3, X5, dY5, dW5, state, ws, n, aidx,
+                                 (s_w, s_m, s_v, s_g), hp, AC["step"], args.warmup + args.steps)
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(np)
+    print(json.dumps(out), flush=True)
+
+
+def verify(torch, np, br, reps, g_red, X3, W3, Y3, X5, dY5, dW5, state, ws, n, aidx, samples, hp, step0, nsteps):
+    """Bit-exactness of the timed run's outputs against the oracle (sampled)."""
+    import oracle
+
+    def differing_words(a, b):
+        a = np.ascontiguousarray(a, np.float32).reshape(-1).view(np.uint32)
+        b = np.ascontiguousarray(b, np.float32).reshape(-1).view(np.uint32)
+        return np.nonzero(a != b)[0]
+
+    t = time.time()
+    res = {}
+    reps_h = [r.cpu().numpy() for r in reps]
+    res["tree_reduce_words_differing"] = int(differing_words(g_red.cpu().numpy(), oracle.tree_reduce(reps_h)).size)
+    del reps_h
+
+    def gemm_rows_cols(A_op, Bt, C, rows, cols):
+        bad = 0
+        for r in rows:
+            bad += differing_words(C[r].cpu().numpy(), oracle.gemm(A_op[r:r + 1], Bt, trans_b=True)[0]).size
+        for c in cols:
+            bad += differing_words(C[:, c].cpu().numpy(), oracle.gemm(A_op, Bt[c:c + 1], trans_b=True)[:, 0]).size
+        return int(bad)
+
+    a3 = X3.cpu().numpy()
+    bt3 = np.ascontiguousarray(W3.cpu().numpy().T)
+    res["gemm_fwd_sampled_words_differing"] = gemm_rows_cols(a3, bt3, Y3, [0, 4097], [8191])
+    a5 = np.ascontiguousarray(X5.cpu().numpy().T)
+    bt5 = np.ascontiguousarray(dY5.cpu().numpy().T)
+    res["gemm_dw_sampled_words_differing"] = gemm_rows_cols(a5, bt5, dW5, [1029], [77])
+    del a3, bt3, a5, bt5
+    # AdamW: replay every step the GPU took on the sampled elements.
+    s_w, s_m, s_v, s_g = samples
+    st = np.concatenate([s_w, s_m, s_v]).astype(np.float32)
+    for t_ in range(step0, step0 + nsteps):
+        oracle.adamw_inplace(st, s_g, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], t_)
+    tidx = torch.from_numpy(aidx).to(state.device)
+    k = aidx.size
+    got = np.concatenate([state[:n][tidx].cpu().numpy(), state[n:2 * n][tidx].cpu().numpy(),
+                          state[2 * n:][tidx].cpu().numpy()])
+    res["adamw_sampled_words_differing"] = int(differing_words(got, st).size)
+    res["adamw_sampled_elements"] = int(k)
+    # Hash: leaf digests of the final state at sampled leaves (level 0 of the workspace).
+    nleaves = (12 * n + 4095) // 4096
+    leaves = sorted({0, 1, nleaves // 3, nleaves // 3 + 1, nleaves - 1} |
+                    set(np.random.default_rng(5).integers(0, nleaves, 27).tolist()))
+    wsh = ws[:32 * nleaves].view(nleaves, 32)
+    bad = 0
+    for leaf in leaves:
+        words = state[leaf * 1024:(leaf + 1) * 1024].cpu().numpy()
+        ref = oracle.state_hash_one_leaf(words, leaf, leaf == nleaves - 1)
+        bad += int(wsh[leaf].cpu().numpy().tobytes() != ref)
+    res["state_hash_sampled_leaves_differing"] = bad
+    res["state_hash_sampled_leaves"] = len(leaves)
+    res["seconds"] = round(time.time() - t, 1)
+    return res
+
+
+def cpu_baseline(np):
+    """The oracle timed on a bounded sample of the same step (one host core)."""
+    import oracle
+    import synth
+    scale = 4  # a quarter of every memory-side workload of the step
+    n_red = synth.REDUCE["n"] // scale
+    n_adam = synth.ADAMW["n"] // scale
+    reps = [synth.reduce_replica(r, n_red) for r in range(8)]
+    st = np.concatenate([synth.adamw_w(n_adam), synth.adamw_m(n_adam), synth.adamw_v(n_adam)])
+    g = synth.adamw_g(n_adam)
+    x = synth.gemm_x(rows=4).reshape(4, 2048)
+    bt = np.ascontiguousarray(synth.gemm_w().reshape(2048, 8192).T)
+    t0 = time.perf_counter()
+    oracle.tree_reduce(reps)
+    t1 = time.perf_counter()
+    oracle.adamw_inplace(st, g, 3e-4, 0.9, 0.999, 1e-8, 0.1, 1000)
+    t2 = time.perf_counter()
+    oracle.state_hash(st)
+    t3 = time.perf_counter()
+    oracle.gemm(x, bt, trans_b=True)
+    t4 = time.perf_counter()
+    nbytes = 9 * 4 * n_red + 28 * n_adam + 12 * n_adam
+    return {"value": round(nbytes / (t3 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "gemm_gflops": round(2 * 4 * 8192 * 2048 / (t4 - t3) / 1e9, 4),
+            "sample": f"a quarter of each memory-side workload: reduce R=8 n={n_red}, adamw + state_hash "
+                      f"n={n_adam}; gemm: 4 rows of 8192x2048x8192; single-threaded oracle, {t4 - t0:.1f} s",
+            "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
+
+
+def _cpu_model():
+    try:
+        with open("/proc/cpuinfo") as fh:
+            for ln in fh:
+                if ln.startswith("model name"):
+                    return ln.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+if __name__ == "__main__":
+    main()

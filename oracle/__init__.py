@@ -35,9 +35,11 @@ def _load():
         lib.oracle_blake2b.argtypes = [vp, i64, ctypes.c_int, vp, vp]
         lib.oracle_state_hash_leaves.argtypes = [vp, i64, i64, i64, vp]
         lib.oracle_state_hash.argtypes = [vp, i64, vp]
+        lib.oracle_state_hash_one_leaf.argtypes = [vp, i64, i64, ctypes.c_int, vp]
         lib.oracle_spec_version.restype = ctypes.c_char_p
         for name in ("oracle_fp32_ops", "oracle_gemm", "oracle_tree_reduce", "oracle_adamw_scalars",
-                     "oracle_adamw", "oracle_blake2b", "oracle_state_hash_leaves", "oracle_state_hash"):
+                     "oracle_adamw", "oracle_blake2b", "oracle_state_hash_leaves", "oracle_state_hash",
+                     "oracle_state_hash_one_leaf"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -172,3 +174,12 @@ def state_hash_leaves(words, leaf0: int, count: int) -> np.ndarray:
     ptr = w.ctypes.data if w.size else np.zeros(1, np.float32).ctypes.data
     _check(_load().oracle_state_hash_leaves(ptr, w.size, leaf0, count, out.ctypes.data), "state_hash_leaves")
     return out
+
+
+def state_hash_one_leaf(words, leaf: int, last: bool) -> bytes:
+    """Digest of one leaf (at most 1024 words) placed at node offset `leaf`."""
+    w = _f32(words).reshape(-1)
+    out = np.zeros(32, dtype=np.uint8)
+    ptr = w.ctypes.data if w.size else np.zeros(1, np.float32).ctypes.data
+    _check(_load().oracle_state_hash_one_leaf(ptr, w.size, leaf, int(last), out.ctypes.data), "state_hash_one_leaf")
+    return out.tobytes()

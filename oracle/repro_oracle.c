@@ -465,6 +465,14 @@ int oracle_state_hash_leaves(const float* words, int64_t n_words, int64_t leaf0,
     return ORACLE_OK;
 }
 
+/* One leaf on its own: `n_words` words (at most 1024) hashed as leaf number
+ * `leaf` of a tree, with the last-node flag when `last` is set. */
+int oracle_state_hash_one_leaf(const float* words, int64_t n_words, int64_t leaf, int last, uint8_t* out32) {
+    if (n_words < 0 || n_words * 4 > SH_LEAF || leaf < 0) return ORACLE_EINVAL;
+    sh_node((const uint8_t*)words, (size_t)n_words * 4, (uint64_t)leaf, 0, last != 0, out32);
+    return ORACLE_OK;
+}
+
 int oracle_state_hash(const float* words, int64_t n_words, uint8_t digest[32]) {
     if (n_words < 0) return ORACLE_EINVAL;
     const uint64_t nbytes = (uint64_t)n_words * 4u;

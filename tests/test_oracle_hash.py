@@ -77,6 +77,13 @@ def test_leaf_digests_match_hashlib():
         assert leaves[i].tobytes() == _node(b[leaf * 4096:(leaf + 1) * 4096], leaf, 0, leaf == 5)
 
 
+def test_one_leaf_entry_matches_the_leaf_level():
+    w = np.random.default_rng(10).standard_normal(7 * 1024 + 100).astype(np.float32)
+    leaves = oracle.state_hash_leaves(w, 0, 8)
+    for i in range(8):
+        assert oracle.state_hash_one_leaf(w[i * 1024:(i + 1) * 1024], i, i == 7) == leaves[i].tobytes()
+
+
 def test_single_changes_move_the_digest():
     w = np.random.default_rng(1).standard_normal(3 * 65536).astype(np.float32)
     d0 = oracle.state_hash(w)
