@@ -80,7 +80,7 @@ const char* repro_strerror(int status) {
 
 int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                        const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream) {
-  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > 2) return REPRO_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > 3) return REPRO_EINVAL;
   if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return REPRO_EINVAL;
   if (M == 0 || N == 0) return REPRO_OK;
   if (C == nullptr || ldc < N) return REPRO_EINVAL;

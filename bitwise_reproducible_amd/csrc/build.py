@@ -31,7 +31,9 @@ COMMON = [f"--offload-arch={ARCH}", "-O3", "-std=c++17", "-fPIC", "-ffp-contract
 SOURCES = {
     "api.cpp": ["-x", "hip"],
     "elementwise.hip": [],
-    "gemm.hip": [],
+    # Keep MFMA results in architectural VGPRs, where v_add_f32 reads them
+    # directly (otherwise each product is first copied out of an AGPR).
+    "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "state_hash.hip": [],
 }
 

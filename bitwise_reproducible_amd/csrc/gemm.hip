@@ -211,6 +211,186 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
     }
 }
 
+// ---------------------------------------------------------------------------
+// Matrix-core multiply, VALU add.
+//
+// v_mfma_f32_32x32x1_2b_f32 with K = 1 computes, for two independent 32x32
+// blocks, D = C + a_i * b_j with one rounding.  With C = -0 (the additive
+// identity of IEEE addition, which keeps the sign of a zero product) every D
+// element is exactly fl(a_i * b_j) under the contract, including the flush
+// rule and signed zeros; this was checked bit for bit against v_mul_f32 on
+// ~10^8 products (random exponents, exact ties, products at +-2^-126,
+// zero and subnormal operands, overflow), and the GEMM parity tests check the
+// result.  No sum is formed inside the matrix core: each product then takes
+// its place in the output's own chain with a v_add_f32, k ascending, so the
+// declared order is unchanged while the multiplies leave the VALU.
+//
+// Lane / register layout of the instruction (per block b = 0, 1): A values
+// come from lanes 32b..32b+31 (row i = lane - 32b), B values from the same
+// lanes (column j = lane - 32b); D[i][j] of block b sits in lane
+// j + 32 * ((i / 4) % 2), register 16b + 4 * (i / 8) + i % 4.
+//
+// Wave tile 64 x 64: lanes 0..63 supply rows 0..63 (block 0 = rows 0..31,
+// block 1 = rows 32..63), both halves of the wave supply the same 32
+// columns, and two instructions cover columns 0..31 and 32..63.  The
+// workgroup is 2 x 2 waves, a 128 x 128 output tile, with BK-deep k slabs
+// staged through LDS exactly as in the VALU kernel.
+typedef float floatx32 __attribute__((ext_vector_type(32)));
+
+template <int BK, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
+                                                   int64_t lda, const float* __restrict__ B, int64_t ldb,
+                                                   float* __restrict__ C, int64_t ldc, int tiles_n) {
+  constexpr int BM = 128, BN = 128, NT = 256, PAD = 4;
+  constexpr int LA = BM * BK / 4 / NT, LB = BK * BN / 4 / NT;
+  static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
+  __shared__ __attribute__((aligned(16))) float As[2][BK][BM + PAD];
+  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + PAD];
+
+  const int tile = blockIdx.x;
+  const int64_t i0 = (int64_t)(tile / tiles_n) * BM;
+  const int64_t j0 = (int64_t)(tile % tiles_n) * BN;
+  const int tid = threadIdx.x;
+  const int lane = tid & 63;
+  const int wave = tid >> 6;
+  const int wm = (wave >> 1) * 64;  // wave's first row inside the tile
+  const int wn = (wave & 1) * 64;   // wave's first column inside the tile
+
+  float4 ra[LA], rb[LB];
+  auto load_slab = [&](int64_t k0) {
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int f = tid + q * NT;
+      if constexpr (!TA) {
+        const int r = f / (BK / 4), c4 = f % (BK / 4);
+        ra[q] = load_chunk<VEC>(A, i0 + r, k0 + 4 * c4, lda, M, K);
+      } else {
+        const int c = f / (BM / 4), r4 = f % (BM / 4);
+        ra[q] = load_chunk<VEC>(A, k0 + c, i0 + 4 * r4, lda, K, M);
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int f = tid + q * NT;
+      if constexpr (!TB) {
+        const int c = f / (BN / 4), j4 = f % (BN / 4);
+        rb[q] = load_chunk<VEC>(B, k0 + c, j0 + 4 * j4, ldb, K, N);
+      } else {
+        const int j = f / (BK / 4), c4 = f % (BK / 4);
+        rb[q] = load_chunk<VEC>(B, j0 + j, k0 + 4 * c4, ldb, N, K);
+      }
+    }
+  };
+  auto store_slab = [&](int buf) {
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int f = tid + q * NT;
+      if constexpr (!TA) {
+        const int r = f / (BK / 4), c4 = f % (BK / 4);
+        As[buf][4 * c4 + 0][r] = ra[q].x;
+        As[buf][4 * c4 + 1][r] = ra[q].y;
+        As[buf][4 * c4 + 2][r] = ra[q].z;
+        As[buf][4 * c4 + 3][r] = ra[q].w;
+      } else {
+        const int c = f / (BM / 4), r4 = f % (BM / 4);
+        *reinterpret_cast<float4*>(&As[buf][c][4 * r4]) = ra[q];
+      }
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int f = tid + q * NT;
+      if constexpr (!TB) {
+        const int c = f / (BN / 4), j4 = f % (BN / 4);
+        *reinterpret_cast<float4*>(&Bs[buf][c][4 * j4]) = rb[q];
+      } else {
+        const int j = f / (BK / 4), c4 = f % (BK / 4);
+        Bs[buf][4 * c4 + 0][j] = rb[q].x;
+        Bs[buf][4 * c4 + 1][j] = rb[q].y;
+        Bs[buf][4 * c4 + 2][j] = rb[q].z;
+        Bs[buf][4 * c4 + 3][j] = rb[q].w;
+      }
+    }
+  };
+
+  floatx32 acc0, acc1, negz;
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    acc0[r] = 0.0f;  // every chain starts at +0
+    acc1[r] = 0.0f;
+    negz[r] = -0.0f;
+  }
+  auto mac_step = [&](int buf, int kk) {
+    const float a = As[buf][kk][wm + lane];
+    const float b0 = Bs[buf][kk][wn + (lane & 31)];
+    const float b1 = Bs[buf][kk][wn + 32 + (lane & 31)];
+    const floatx32 p0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, negz, 0, 0, 0);
+    const floatx32 p1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b1, negz, 0, 0, 0);
+#pragma unroll
+    for (int r = 0; r < 32; ++r) acc0[r] = acc0[r] + p0[r];
+#pragma unroll
+    for (int r = 0; r < 32; ++r) acc1[r] = acc1[r] + p1[r];
+  };
+
+  const int64_t nslabs = (K + BK - 1) / BK;
+  if (nslabs > 0) {
+    load_slab(0);
+    store_slab(0);
+    __syncthreads();
+    for (int64_t s = 0; s < nslabs; ++s) {
+      const int buf = (int)(s & 1);
+      if (s + 1 < nslabs) load_slab((s + 1) * BK);
+      const int64_t kleft = K - s * BK;
+      if (kleft >= BK) {
+#pragma unroll
+        for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
+      } else {
+        for (int kk = 0; kk < (int)kleft; ++kk) mac_step(buf, kk);
+      }
+      if (s + 1 < nslabs) store_slab(buf ^ 1);
+      __syncthreads();
+    }
+  }
+
+  // Register r of a lane holds row 32*(r/16) + 8*((r%16)/4) + 4*(lane/32) + r%4
+  // of the wave tile, column lane%32 (+32 for the second instruction).
+  const int64_t col0 = j0 + wn + (lane & 31);
+#pragma unroll
+  for (int r = 0; r < 32; ++r) {
+    const int rr = r & 15;
+    const int64_t row = i0 + wm + 32 * (r >> 4) + 8 * (rr >> 2) + 4 * (lane >> 5) + (rr & 3);
+    if (row < M) {
+      if (col0 < N) C[row * ldc + col0] = acc0[r];
+      if (col0 + 32 < N) C[row * ldc + col0 + 32] = acc1[r];
+    }
+  }
+}
+
+template <int BK, bool TA, bool TB, bool VEC>
+hipError_t launch_mfma(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
+                       float* C, int64_t ldc, hipStream_t stream) {
+  const int64_t tiles_m = (M + 127) / 128;
+  const int64_t tiles_n = (N + 127) / 128;
+  const int64_t tiles = tiles_m * tiles_n;
+  if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  hipLaunchKernelGGL((k_gemm_mfma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A, lda,
+                     B, ldb, C, ldc, (int)tiles_n);
+  return hipGetLastError();
+}
+
+hipError_t dispatch_mfma(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                         const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
+#define REPRO_GEMM_CASE(TA_, TB_)                                                                 \
+  if (ta == TA_ && tb == TB_)                                                                     \
+    return vec ? launch_mfma<16, TA_, TB_, true>(M, N, K, A, lda, B, ldb, C, ldc, stream)         \
+               : launch_mfma<16, TA_, TB_, false>(M, N, K, A, lda, B, ldb, C, ldc, stream);
+  REPRO_GEMM_CASE(0, 0)
+  REPRO_GEMM_CASE(1, 0)
+  REPRO_GEMM_CASE(0, 1)
+  REPRO_GEMM_CASE(1, 1)
+#undef REPRO_GEMM_CASE
+  return hipErrorInvalidValue;
+}
+
 template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
 hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                         int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
@@ -252,6 +432,7 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   const bool vec = variant != 1 && al16(A) && al16(B) && lda % 4 == 0 && ldb % 4 == 0 && a_contig % 4 == 0 &&
                    b_contig % 4 == 0;
   if (variant == 2) return dispatch<64, 64, 16, 4, 4>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  if (variant == 3) return dispatch_mfma(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   return dispatch<128, 128, 16, 8, 8>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 

@@ -83,9 +83,12 @@ const char* repro_strerror(int status);
 int repro_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                const float* B, int64_t ldb, float* C, int64_t ldc, void* stream);
 
-/* As repro_gemm with an explicit kernel variant: 0 is the default; 1 uses
- * scalar global loads; 2 uses a 64x64 output tile.  All variants return the
- * same bits; they exist to test that claim. */
+/* As repro_gemm with an explicit kernel variant: 0 is the default (VALU
+ * multiply and add, 128x128 tile); 1 uses scalar global loads; 2 uses a
+ * 64x64 output tile; 3 forms each product fl(a*b) on the matrix cores
+ * (v_mfma_f32_32x32x1_2b_f32 with K = 1 and C = -0, one product per output
+ * element, nothing summed inside) and adds it into the output's chain on the
+ * VALU.  All variants return the same bits; they exist to test that claim. */
 int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A,
                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant,
                        void* stream);

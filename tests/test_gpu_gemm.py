@@ -37,7 +37,7 @@ def test_shapes_transposes_variants(M, N, K, ta, tb):
     A, B = _stored(M, N, K, ta, tb, 0x8000 + M + 7 * N + 13 * K)
     ref = oracle.gemm(A, B, bool(ta), bool(tb))
     dA, dB = to_dev(A), to_dev(B)
-    for variant in (0, 1, 2):
+    for variant in (0, 1, 2, 3):
         C = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=variant)
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
