@@ -37,12 +37,14 @@ FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
 # the same rate (measured), which bounds the hash.
 VALU_LANE_OPS = 256 * 128 * 2.4e9
 GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
-# BLAKE2b: per 128-byte block 12 rounds x 8 G; a G is 6 64-bit adds (2
-# lane-ops each), 4 64-bit xors (2 each) and 3 rotations by 24/16/63 (2 each;
-# the rotation by 32 is a register swap): 26 lane-ops, plus 16 xors for the
-# feed-forward: 2512 lane-ops per 128 bytes.
-HASH_OPS_PER_BYTE = (12 * 8 * 26 + 16) / 128
-HASH_PEAK_GBS = VALU_LANE_OPS / HASH_OPS_PER_BYTE / 1e9
+# BLAKE2b: per 128-byte block 12 rounds x 8 G.  In issue slots of the
+# 32-bit VALU: a G is 6 64-bit adds (v_add_co + v_addc, 2 slots each), 4
+# 64-bit xors (2 slots each) and 3 rotations by 24/16/63 (two v_alignbit_b32
+# each; 3-operand VOP3 ops issue at half rate on gfx950, measured, so 4
+# slots); the rotation by 32 is a register swap.  32 slots per G, plus 16
+# xors of the feed-forward: 3088 slots per 128 bytes.
+HASH_SLOTS_PER_BYTE = (12 * 8 * 32 + 16) / 128
+HASH_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
 
 
 def log(*a):
@@ -202,7 +204,7 @@ def main():
                     "frac_of_fp32_vector_peak": round(ach / FP32_VECTOR_PEAK, 4)}
         b = {"tree_reduce": bytes_reduce, "adamw": bytes_adamw, "state_hash": bytes_hash}[op]
         ach = b / (ms * 1e-3) / 1e9
-        if op == "state_hash":  # integer-VALU bound: ~19.6 lane-ops per byte
+        if op == "state_hash":  # integer-VALU bound: ~24 issue slots per byte
             return {"bound": "alu", "achieved": round(ach, 1), "peak": round(HASH_PEAK_GBS, 1), "unit": "GB/s",
                     "frac": round(ach / HASH_PEAK_GBS, 4), "traffic": None,
                     "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4)}
