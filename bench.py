@@ -47,6 +47,30 @@ HASH_SLOTS_PER_BYTE = (12 * 8 * 32 + 16) / 128
 HASH_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
 
 
+def recorded_traffic():
+    """HBM bytes per launch from the committed rocprofv3 counter summary, per
+    op, kept only while the kernel source is the one the counters came from."""
+    import hashlib
+    path = os.path.join(ROOT, "profiles", "pmc_traffic_bench_step.md")
+    out = {}
+    try:
+        lines = open(path).read().splitlines()
+    except OSError:
+        return out
+    for ln in lines:
+        parts = ln.split()
+        if len(parts) == 5 and parts[0] == "traffic":
+            _, op, nbytes, src, sha = parts
+            cur = os.path.join(ROOT, "bitwise_reproducible_amd", "csrc", src)
+            try:
+                now = hashlib.sha256(open(cur, "rb").read()).hexdigest()[:16]
+            except OSError:
+                continue
+            if now == sha:
+                out[op] = int(nbytes)
+    return out
+
+
 def log(*a):
     print("[bench]", *a, file=sys.stderr, flush=True)
 
@@ -58,6 +82,9 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-verify", action="store_true", help="skip the oracle check after timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--calibration-copy", action="store_true",
+                   help="after timing, run one plain copy of 64 MiB (a one-replica fold without the average) whose "
+                        "HBM counters calibrate the FETCH_SIZE / WRITE_SIZE readings of a profiling run")
     return p.parse_args()
 
 
@@ -183,6 +210,10 @@ def main():
     op_ms = {op: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
              for i, op in enumerate(ops)}
 
+    if args.calibration_copy:
+        br.repro_tree_reduce([reps[0]], out=g_red, average=False)
+        torch.cuda.synchronize()
+
     # Algorithmic work per launch.
     bytes_reduce = (RC["R"] + 1) * 4 * RC["n"]
     bytes_adamw = 28 * n
@@ -212,6 +243,10 @@ def main():
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
 
     per_op = {op: {"ms": round(op_ms[op], 4), **roof(op)} for op in ops}
+    traffic = recorded_traffic()
+    for op in ops:
+        key = "state_hash_leaves" if op == "state_hash" else op
+        per_op[op]["traffic"] = traffic.get(key)
     dominant = max(ops, key=lambda o: op_ms[o])
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,

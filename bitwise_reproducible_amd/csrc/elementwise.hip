@@ -103,17 +103,31 @@ __device__ __forceinline__ V tree_fold(const V* x) {
 
 static_assert(REPRO_MAX_REPLICAS <= 127, "fold_rest walks bits 0..6");
 
-// One 16-byte vector per replica per iteration.
-template <int R>
+// One 16-byte vector per replica per thread (the grid covers all n/4
+// vectors; measured on MI355X this shape streams faster than a grid-stride
+// loop).  AVG selects the multiply by fl(1/R) at compile time.
+template <int R, bool AVG>
 __global__ __launch_bounds__(256) void k_tree_reduce_v4(ReplicaPtrs reps, float4* __restrict__ out, int64_t n4,
-                                                         float rR, int average) {
+                                                         float rR) {
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float4 x[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) x[r] = ld_nt(reinterpret_cast<const float4*>(reps.p[r]) + i);
+  float4 s = tree_fold<R>(x);
+  if constexpr (AVG) s = mul4s(s, rR);
+  st_nt(s, out + i);
+}
+
+// The same with a grid-stride loop over a capped grid (launch-shape variant).
+template <int R>
+__global__ __launch_bounds__(256) void k_tree_reduce_v4_strided(ReplicaPtrs reps, float4* __restrict__ out,
+                                                                 int64_t n4, float rR, int average) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
     float4 x[R];
 #pragma unroll
-    for (int r = 0; r < R; ++r) {
-      x[r] = ld_nt(reinterpret_cast<const float4*>(reps.p[r]) + i);
-    }
+    for (int r = 0; r < R; ++r) x[r] = ld_nt(reinterpret_cast<const float4*>(reps.p[r]) + i);
     float4 s = tree_fold<R>(x);
     if (average) s = mul4s(s, rR);
     st_nt(s, out + i);
@@ -135,19 +149,26 @@ __global__ __launch_bounds__(256) void k_tree_reduce_s(ReplicaPtrs reps, float* 
   }
 }
 
-using V4Fn = void (*)(ReplicaPtrs, float4*, int64_t, float, int);
+using V4Fn = void (*)(ReplicaPtrs, float4*, int64_t, float);
+using V4SFn = void (*)(ReplicaPtrs, float4*, int64_t, float, int);
 using SFn = void (*)(ReplicaPtrs, float*, int64_t, int64_t, float, int);
 
-template <int... Rs>
+template <bool AVG, int... Rs>
 constexpr auto make_v4_table(std::integer_sequence<int, Rs...>) {
-  return std::array<V4Fn, sizeof...(Rs)>{{&k_tree_reduce_v4<Rs + 1>...}};
+  return std::array<V4Fn, sizeof...(Rs)>{{&k_tree_reduce_v4<Rs + 1, AVG>...}};
+}
+template <int... Rs>
+constexpr auto make_v4s_table(std::integer_sequence<int, Rs...>) {
+  return std::array<V4SFn, sizeof...(Rs)>{{&k_tree_reduce_v4_strided<Rs + 1>...}};
 }
 template <int... Rs>
 constexpr auto make_s_table(std::integer_sequence<int, Rs...>) {
   return std::array<SFn, sizeof...(Rs)>{{&k_tree_reduce_s<Rs + 1>...}};
 }
 
-const auto kV4Table = make_v4_table(std::make_integer_sequence<int, REPRO_MAX_REPLICAS>{});
+const auto kV4Table = make_v4_table<false>(std::make_integer_sequence<int, REPRO_MAX_REPLICAS>{});
+const auto kV4AvgTable = make_v4_table<true>(std::make_integer_sequence<int, REPRO_MAX_REPLICAS>{});
+const auto kV4StridedTable = make_v4s_table(std::make_integer_sequence<int, REPRO_MAX_REPLICAS>{});
 const auto kSTable = make_s_table(std::make_integer_sequence<int, REPRO_MAX_REPLICAS>{});
 
 int64_t grid_for(int64_t items, int threads, int64_t cap) {
@@ -186,20 +207,19 @@ __device__ __forceinline__ void adamw_elem(float& w, float& m, float& v, float g
 __global__ __launch_bounds__(256) void k_adamw_v4(float4* __restrict__ w4, float4* __restrict__ m4,
                                                    float4* __restrict__ v4, const float4* __restrict__ g4,
                                                    int64_t n4, AdamwScalars s) {
-  const int64_t stride = (int64_t)gridDim.x * blockDim.x;
-  for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n4; i += stride) {
-    float4 w = ld_nt(w4 + i);
-    float4 m = ld_nt(m4 + i);
-    float4 v = ld_nt(v4 + i);
-    const float4 g = ld_nt(g4 + i);
-    adamw_elem(w.x, m.x, v.x, g.x, s);
-    adamw_elem(w.y, m.y, v.y, g.y, s);
-    adamw_elem(w.z, m.z, v.z, g.z, s);
-    adamw_elem(w.w, m.w, v.w, g.w, s);
-    st_nt(w, w4 + i);
-    st_nt(m, m4 + i);
-    st_nt(v, v4 + i);
-  }
+  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (i >= n4) return;
+  float4 w = ld_nt(w4 + i);
+  float4 m = ld_nt(m4 + i);
+  float4 v = ld_nt(v4 + i);
+  const float4 g = ld_nt(g4 + i);
+  adamw_elem(w.x, m.x, v.x, g.x, s);
+  adamw_elem(w.y, m.y, v.y, g.y, s);
+  adamw_elem(w.z, m.z, v.z, g.z, s);
+  adamw_elem(w.w, m.w, v.w, g.w, s);
+  st_nt(w, w4 + i);
+  st_nt(m, m4 + i);
+  st_nt(v, v4 + i);
 }
 
 __global__ __launch_bounds__(256) void k_adamw_s(float* __restrict__ w, float* __restrict__ m,
@@ -243,10 +263,15 @@ hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* 
   for (int r = 0; r < R; ++r) vec = vec && aligned16(reps.p[r]);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {
-    const int threads = variant == 2 ? 64 : 256;
-    const int64_t grid = variant == 2 ? grid_for(n4, threads, 1024) : grid_for(n4, threads, int64_t(1) << 20);
-    hipLaunchKernelGGL(kV4Table[R - 1], dim3((unsigned)grid), dim3(threads), 0, stream, reps,
-                       reinterpret_cast<float4*>(out), n4, rR, average);
+    if (variant == 2) {
+      hipLaunchKernelGGL(kV4StridedTable[R - 1], dim3((unsigned)grid_for(n4, 64, 1024)), dim3(64), 0, stream, reps,
+                         reinterpret_cast<float4*>(out), n4, rR, average);
+    } else {
+      const int64_t grid = (n4 + 255) / 256;
+      if (grid > 0x7fffffff) return hipErrorInvalidValue;
+      hipLaunchKernelGGL((average ? kV4AvgTable : kV4Table)[R - 1], dim3((unsigned)grid), dim3(256), 0, stream,
+                         reps, reinterpret_cast<float4*>(out), n4, rR);
+    }
   }
   const int64_t first = n4 * 4;
   if (first < n) {
@@ -265,7 +290,8 @@ hipError_t launch_adamw(float* state, const float* grad, int64_t n, const AdamwS
   const bool vec = variant != 1 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(grad);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {
-    const int64_t grid = grid_for(n4, 256, int64_t(1) << 20);
+    const int64_t grid = (n4 + 255) / 256;
+    if (grid > 0x7fffffff) return hipErrorInvalidValue;
     hipLaunchKernelGGL(k_adamw_v4, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<float4*>(w),
                        reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v),
                        reinterpret_cast<const float4*>(grad), n4, s);
