@@ -329,13 +329,13 @@ def cpu_baseline(np):
     """The oracle timed on a bounded sample of the same step (one host core)."""
     import oracle
     import synth
-    scale = 4  # a quarter of every memory-side workload of the step
+    scale = 2  # half of every memory-side workload of the step
     n_red = synth.REDUCE["n"] // scale
     n_adam = synth.ADAMW["n"] // scale
     reps = [synth.reduce_replica(r, n_red) for r in range(8)]
     st = np.concatenate([synth.adamw_w(n_adam), synth.adamw_m(n_adam), synth.adamw_v(n_adam)])
     g = synth.adamw_g(n_adam)
-    x = synth.gemm_x(rows=4).reshape(4, 2048)
+    x = synth.gemm_x(rows=16).reshape(16, 2048)
     bt = np.ascontiguousarray(synth.gemm_w().reshape(2048, 8192).T)
     t0 = time.perf_counter()
     oracle.tree_reduce(reps)
@@ -348,9 +348,9 @@ def cpu_baseline(np):
     t4 = time.perf_counter()
     nbytes = 9 * 4 * n_red + 28 * n_adam + 12 * n_adam
     return {"value": round(nbytes / (t3 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "gemm_gflops": round(2 * 4 * 8192 * 2048 / (t4 - t3) / 1e9, 4),
-            "sample": f"a quarter of each memory-side workload: reduce R=8 n={n_red}, adamw + state_hash "
-                      f"n={n_adam}; gemm: 4 rows of 8192x2048x8192; single-threaded oracle, {t4 - t0:.1f} s",
+            "gemm_gflops": round(2 * 16 * 8192 * 2048 / (t4 - t3) / 1e9, 4),
+            "sample": f"half of each memory-side workload: reduce R=8 n={n_red}, adamw + state_hash "
+                      f"n={n_adam}; gemm: 16 rows of 8192x2048x8192; single-threaded oracle, {t4 - t0:.1f} s",
             "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
 
 

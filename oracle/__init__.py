@@ -30,6 +30,9 @@ def _load():
         lib.oracle_fp32_ops.argtypes = [ctypes.c_int, vp, vp, vp, i64]
         lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
         lib.oracle_tree_reduce.argtypes = [vp, i32, i64, vp, i32, vp]
+        lib.oracle_replay_reduce.argtypes = [vp, i32, i32, i32, i64, vp]
+        lib.oracle_fold_push.argtypes = [vp, i32, vp, i64]
+        lib.oracle_fold_result.argtypes = [vp, i32, i64, vp, i32]
         lib.oracle_adamw_scalars.argtypes = [f32, f32, i64, vp]
         lib.oracle_adamw.argtypes = [vp, vp, i64, f32, f32, f32, f32, f32, i64]
         lib.oracle_blake2b.argtypes = [vp, i64, ctypes.c_int, vp, vp]
@@ -39,7 +42,8 @@ def _load():
         lib.oracle_spec_version.restype = ctypes.c_char_p
         for name in ("oracle_fp32_ops", "oracle_gemm", "oracle_tree_reduce", "oracle_adamw_scalars",
                      "oracle_adamw", "oracle_blake2b", "oracle_state_hash_leaves", "oracle_state_hash",
-                     "oracle_state_hash_one_leaf"):
+                     "oracle_state_hash_one_leaf", "oracle_replay_reduce", "oracle_fold_push",
+                     "oracle_fold_result"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -183,3 +187,34 @@ def state_hash_one_leaf(words, leaf: int, last: bool) -> bytes:
     ptr = w.ctypes.data if w.size else np.zeros(1, np.float32).ctypes.data
     _check(_load().oracle_state_hash_one_leaf(ptr, w.size, leaf, int(last), out.ctypes.data), "state_hash_one_leaf")
     return out.tobytes()
+
+
+def replay_reduce(grads, dp_replicate: int, dp_shard: int, accum: int) -> np.ndarray:
+    """Algorithm 1's reduction: grads in mesh order, rank-major then microbatch."""
+    bufs = [_f32(g).reshape(-1) for g in grads]
+    assert len(bufs) == dp_replicate * dp_shard * accum
+    n = bufs[0].size
+    assert all(b.size == n for b in bufs)
+    ptrs = (ctypes.c_void_p * len(bufs))(*[b.ctypes.data for b in bufs])
+    out = np.empty(n, dtype=np.float32)
+    _check(_load().oracle_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), dp_replicate, dp_shard, accum, n,
+                                        out.ctypes.data), "replay_reduce")
+    return out
+
+
+def fold_push(slots, pushed: int, part) -> None:
+    """Streaming TreeFold push into a list of numpy level slots (modified in place)."""
+    p = _f32(part).reshape(-1)
+    for sl in slots:
+        assert sl.dtype == np.float32 and sl.flags.c_contiguous and sl.size == p.size
+    ptrs = (ctypes.c_void_p * len(slots))(*[sl.ctypes.data for sl in slots])
+    _check(_load().oracle_fold_push(ctypes.cast(ptrs, ctypes.c_void_p), pushed, p.ctypes.data, p.size), "fold_push")
+
+
+def fold_result(slots, pushed: int, divisor: int = 0) -> np.ndarray:
+    n = slots[0].size
+    ptrs = (ctypes.c_void_p * len(slots))(*[sl.ctypes.data for sl in slots])
+    out = np.empty(n, dtype=np.float32)
+    _check(_load().oracle_fold_result(ctypes.cast(ptrs, ctypes.c_void_p), pushed, n, out.ctypes.data, divisor),
+           "fold_result")
+    return out

@@ -205,6 +205,110 @@ int oracle_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float
 }
 
 /* ------------------------------------------------------------------------ */
+/* Audit replay of one step's gradient reduction (section 6, Algorithm 1, with
+ * Appendix A.1-A.3).  N = dp_replicate * dp_shard virtual ranks in mesh order
+ * (r = rep * dp_shard + shard); rank r has `accum` microbatch gradients,
+ * grads[r * accum + k].  For every rank: g_r = 0, then for each microbatch
+ * g_r = g_r + grad * fl(1/accum).  The shards of a replica are summed in
+ * ascending shard order (inner = g_0, then inner = inner + g_s), the sum is
+ * multiplied by fl(1/dp_shard) and pushed into the TreeFold; at the end the
+ * fold's Result is multiplied by fl(1/dp_replicate).  Every "/" of the
+ * algorithm is this multiply by a host-computed binary32 reciprocal
+ * (Appendix A.3). */
+int oracle_replay_reduce(const float* const* grads, int32_t dp_replicate, int32_t dp_shard, int32_t accum,
+                         int64_t n, float* out) {
+    if (dp_replicate < 1 || dp_shard < 1 || accum < 1 || n < 0 || grads == NULL) return ORACLE_EINVAL;
+    const int64_t N = (int64_t)dp_replicate * dp_shard;
+    for (int64_t b = 0; b < N * accum; ++b) if (n > 0 && grads[b] == NULL) return ORACLE_EINVAL;
+    if (n == 0) return ORACLE_OK;
+    fpenv_t e = enter_contract();
+    const float r_accum = f_div(1.0f, (float)accum);
+    const float r_shard = f_div(1.0f, (float)dp_shard);
+    const float r_rep = f_div(1.0f, (float)dp_replicate);
+    treefold_t f;
+    f.capacity = 40;
+    f.stack = (fold_entry_t*)calloc((size_t)f.capacity, sizeof(fold_entry_t));
+    f.depth = 0;
+    f.max_depth = 0;
+    f.n = n;
+    float* g = (float*)malloc((size_t)n * sizeof(float));
+    float* inner = NULL;
+    if (!f.stack || !g) { free(f.stack); free(g); leave_contract(e); return ORACLE_ENOMEM; }
+    for (int64_t r = 0; r < N; ++r) {
+        const int64_t shard = r % dp_shard;
+        for (int64_t i = 0; i < n; ++i) g[i] = 0.0f;
+        for (int32_t k = 0; k < accum; ++k) {
+            const float* x = grads[r * accum + k];
+            for (int64_t i = 0; i < n; ++i) g[i] = f_add(g[i], f_mul(x[i], r_accum));
+        }
+        if (shard == 0) {
+            inner = (float*)malloc((size_t)n * sizeof(float));
+            if (!inner) { free(g); leave_contract(e); return ORACLE_ENOMEM; }
+            for (int64_t i = 0; i < n; ++i) inner[i] = g[i];
+        } else {
+            for (int64_t i = 0; i < n; ++i) inner[i] = f_add(inner[i], g[i]);
+        }
+        if (shard == dp_shard - 1) {
+            for (int64_t i = 0; i < n; ++i) inner[i] = f_mul(inner[i], r_shard);
+            fold_push(&f, inner); /* the fold owns `inner` from here */
+            inner = NULL;
+        }
+    }
+    float* acc = fold_result(&f);
+    for (int64_t i = 0; i < n; ++i) out[i] = f_mul(acc[i], r_rep);
+    free(acc);
+    free(g);
+    free(f.stack);
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* TreeFold as a streaming interface over caller-owned level slots (Appendix
+ * A.1: at most floor(log2 R) + 1 partials resident).  slots[L] holds the
+ * stack entry of level L, which exists exactly when bit L of `pushed` (the
+ * number of partials pushed so far) is set.  Push combines the incoming
+ * partial with the entries of levels 0, 1, ... while those bits are set
+ * (lower block on the left) and stores the result in the first free level. */
+int oracle_fold_push(float* const* slots, int32_t pushed, const float* part, int64_t n) {
+    if (pushed < 0 || n < 0 || slots == NULL || (n > 0 && part == NULL)) return ORACLE_EINVAL;
+    fpenv_t e = enter_contract();
+    int level = 0;
+    float* carry = (float*)malloc((size_t)(n > 0 ? n : 1) * sizeof(float));
+    if (!carry) { leave_contract(e); return ORACLE_ENOMEM; }
+    for (int64_t i = 0; i < n; ++i) carry[i] = part[i];
+    while ((pushed >> level) & 1) {
+        for (int64_t i = 0; i < n; ++i) carry[i] = f_add(slots[level][i], carry[i]);
+        ++level;
+    }
+    for (int64_t i = 0; i < n; ++i) slots[level][i] = carry[i];
+    free(carry);
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* Result after `pushed` partials: start from the lowest occupied level and
+ * add the others in ascending level order; multiply by fl(1/divisor) when
+ * divisor > 0. */
+int oracle_fold_result(float* const* slots, int32_t pushed, int64_t n, float* out, int32_t divisor) {
+    if (pushed < 1 || n < 0 || slots == NULL || divisor < 0) return ORACLE_EINVAL;
+    fpenv_t e = enter_contract();
+    int level = 0;
+    while (((pushed >> level) & 1) == 0) ++level;
+    for (int64_t i = 0; i < n; ++i) out[i] = slots[level][i];
+    for (int L = level + 1; L < 31; ++L) {
+        if ((pushed >> L) & 1) {
+            for (int64_t i = 0; i < n; ++i) out[i] = f_add(out[i], slots[L][i]);
+        }
+    }
+    if (divisor > 0) {
+        const float r = f_div(1.0f, (float)divisor);
+        for (int64_t i = 0; i < n; ++i) out[i] = f_mul(out[i], r);
+    }
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
 /* AdamW (Loshchilov and Hutter), as the fused FP32 optimizer step of the
  * OPEN-1B recipe, section 3.2.  State is one flat array [w | m | v] of 3n
  * binary32 words (checkpoint page, "file format"); grad has n words.

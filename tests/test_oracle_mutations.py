@@ -16,6 +16,7 @@ import test_oracle_adamw as T_ADAMW
 import test_oracle_fp32 as T_FP32
 import test_oracle_gemm as T_GEMM
 import test_oracle_hash as T_HASH
+import test_oracle_replay as T_REPLAY
 import test_oracle_tree_reduce as T_TREE
 
 SRC = oracle_build.SRC
@@ -39,6 +40,16 @@ MUTATIONS = [
      [lambda: T_TREE.test_treefold_equals_recursive_doubling(8)]),
     ("tree_divides", "out[i] = f_mul(acc[i], rR);", "out[i] = f_div(acc[i], (float)R);",
      [lambda: T_TREE.test_average_is_reciprocal_multiply_not_division(3)]),
+    ("replay_microbatch_unscaled", "for (int64_t i = 0; i < n; ++i) g[i] = f_add(g[i], f_mul(x[i], r_accum));",
+     "for (int64_t i = 0; i < n; ++i) g[i] = f_add(g[i], x[i]);",
+     [lambda: T_REPLAY.test_integer_gradients_give_the_exact_mean(2, 4, 2)]),
+    ("replay_shard_divides", "for (int64_t i = 0; i < n; ++i) inner[i] = f_mul(inner[i], r_shard);",
+     "for (int64_t i = 0; i < n; ++i) inner[i] = f_div(inner[i], (float)dp_shard);",
+     [T_REPLAY.test_every_average_is_a_reciprocal_multiply]),
+    ("replay_microbatch_major_buffers", "const float* x = grads[r * accum + k];", "const float* x = grads[k * N + r];",
+     [T_REPLAY.test_buffers_are_rank_major_then_microbatch]),
+    ("fold_push_skips_carry", "while ((pushed >> level) & 1) {", "while (0) {",
+     [lambda: T_REPLAY.test_streaming_push_result_equals_treefold(6)]),
     ("adamw_eps_inside_root", "const float d = f_add(sq, eps);", "const float d = f_sqrt(f_add(vh, eps));",
      [T_ADAMW.test_first_step_closed_form, T_ADAMW.test_constant_gradient_trajectory]),
     ("adamw_no_bias_correction_m", "const float mh = f_mul(mn, s.r1);", "const float mh = mn;",
