@@ -8,6 +8,8 @@ HIP kernels; there is no fallback, and a missing library is an error.
 Entry points (same names as the C ABI):
     repro_gemm(A, B, trans_a=False, trans_b=False, out=None)
     repro_tree_reduce(replicas, out=None, average=True)
+    repro_replay_reduce(grads, dp_replicate, dp_shard, accum, out=None)
+    repro_fold_push(slots, pushed, part);  repro_fold_result(slots, pushed, out, divisor=0)
     repro_adamw(state, grad, lr, beta1, beta2, eps, weight_decay, step)
     repro_state_hash(words, workspace=None) -> 32-byte digest (bytes)
     repro_state_hash_async(words, digest_out, workspace)
@@ -23,6 +25,8 @@ LIB_PATH = os.path.join(_HERE, "librepro.so")
 _lib = None
 
 REPRO_MAX_REPLICAS = 64
+REPRO_MAX_REPLAY_BUFFERS = 384
+REPRO_FOLD_SLOTS = 7
 
 
 class ReproError(RuntimeError):
@@ -56,8 +60,12 @@ def library():
         lib.repro_state_hash_workspace_bytes.argtypes = [i64]
         lib.repro_state_hash.argtypes = [vp, i64, vp, i64, vp, vp]
         lib.repro_fp32_ops.argtypes = [i32, vp, vp, vp, i64, vp]
+        lib.repro_replay_reduce.argtypes = [vp, i32, i32, i32, i64, vp, vp]
+        lib.repro_fold_push.argtypes = [vp, i32, vp, i64, vp]
+        lib.repro_fold_result.argtypes = [vp, i32, i64, vp, i32, vp]
         for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
-                     "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops"):
+                     "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops",
+                     "repro_replay_reduce", "repro_fold_push", "repro_fold_result"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -154,6 +162,49 @@ def repro_tree_reduce(replicas, out=None, average: bool = True, variant: int = 0
     return out
 
 
+def _contiguous_f32(ts, name):
+    n = ts[0].numel()
+    for i, t in enumerate(ts):
+        _f32_device(t, f"{name}[{i}]")
+        if t.numel() != n or not t.is_contiguous():
+            raise ValueError(f"{name} must be contiguous and of equal size")
+    return n
+
+
+def repro_replay_reduce(grads, dp_replicate: int, dp_shard: int, accum: int, out=None, stream=None):
+    """Algorithm 1's reduction of dp_replicate * dp_shard * accum microbatch gradients (mesh order)."""
+    import torch
+    gs = list(grads)
+    if len(gs) != dp_replicate * dp_shard * accum or not gs:
+        raise ValueError("need dp_replicate * dp_shard * accum gradient buffers")
+    n = _contiguous_f32(gs, "grads")
+    if out is None:
+        out = torch.empty_like(gs[0])
+    _contiguous_f32([gs[0], out], "out")
+    ptrs = (ctypes.c_void_p * len(gs))(*[g.data_ptr() for g in gs])
+    _check(library().repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), dp_replicate, dp_shard, accum, n,
+                                         out.data_ptr(), _stream(stream)), "repro_replay_reduce")
+    return out
+
+
+def _slot_ptrs(slots):
+    ptrs = [s.data_ptr() if s is not None else None for s in slots]
+    ptrs += [None] * (REPRO_FOLD_SLOTS - len(ptrs))
+    return (ctypes.c_void_p * REPRO_FOLD_SLOTS)(*ptrs)
+
+
+def repro_fold_push(slots, pushed: int, part, stream=None):
+    """Push one partial into the caller-owned level slots (list of device tensors or None)."""
+    _check(library().repro_fold_push(ctypes.cast(_slot_ptrs(slots), ctypes.c_void_p), int(pushed), part.data_ptr(),
+                                     part.numel(), _stream(stream)), "repro_fold_push")
+
+
+def repro_fold_result(slots, pushed: int, out, divisor: int = 0, stream=None):
+    _check(library().repro_fold_result(ctypes.cast(_slot_ptrs(slots), ctypes.c_void_p), int(pushed), out.numel(),
+                                       out.data_ptr(), int(divisor), _stream(stream)), "repro_fold_result")
+    return out
+
+
 def repro_adamw(state, grad, lr: float, beta1: float, beta2: float, eps: float, weight_decay: float, step: int,
                 variant: int = 0, stream=None):
     """In-place AdamW step on the flat state [w | m | v] (3n floats)."""
@@ -224,6 +275,6 @@ def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
     return out
 
 
-__all__ = ["repro_gemm", "repro_tree_reduce", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
+__all__ = ["repro_gemm", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
            "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
            "ReproError", "LIB_PATH"]

@@ -39,6 +39,12 @@ float replica_reciprocal(int R) {
   return HostFp32::div(1.0f, (float)R);
 }
 
+// fl(1 / d) on the host (Appendix A.3).
+float reciprocal(int d) {
+  HostFp32 env;
+  return HostFp32::div(1.0f, (float)d);
+}
+
 // AdamW host scalars: c = 1 - beta, beta^step as step-1 serial products, and
 // the reciprocals of the bias corrections.
 AdamwScalars adamw_scalars(float lr, float beta1, float beta2, float eps, float wd, int64_t step) {
@@ -120,6 +126,58 @@ int repro_tree_reduce_variant(const float* const* replicas, int32_t R, int64_t n
 int repro_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float* out, int32_t average,
                       void* stream) {
   return repro_tree_reduce_variant(replicas, R, n, out, average, 0, stream);
+}
+
+int repro_replay_reduce(const float* const* grads, int32_t dp_replicate, int32_t dp_shard, int32_t accum,
+                        int64_t n, float* out, void* stream) {
+  if (grads == nullptr || dp_replicate < 1 || dp_replicate > REPRO_MAX_REPLICAS || dp_shard < 1 || accum < 1 ||
+      n < 0)
+    return REPRO_EINVAL;
+  const int64_t nbuf = (int64_t)dp_replicate * dp_shard * accum;
+  if (nbuf > REPRO_MAX_REPLAY_BUFFERS) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (out == nullptr) return REPRO_EINVAL;
+  repro::ReplayPtrs a = {};
+  for (int64_t b = 0; b < nbuf; ++b) {
+    if (grads[b] == nullptr) return REPRO_EINVAL;
+    if (!aligned4(grads[b])) return REPRO_EALIGN;
+    a.p[b] = grads[b];
+  }
+  if (!aligned4(out)) return REPRO_EALIGN;
+  return status_of(repro::launch_replay(a, (int)nbuf, dp_replicate, dp_shard, accum, reciprocal(accum),
+                                        reciprocal(dp_shard), reciprocal(dp_replicate), n, out,
+                                        static_cast<hipStream_t>(stream)));
+}
+
+int repro_fold_push(float* const* slots, int32_t pushed, const float* part, int64_t n, void* stream) {
+  if (slots == nullptr || pushed < 0 || pushed > 126 || n < 0) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (part == nullptr) return REPRO_EINVAL;
+  const int t = __builtin_ctz(~(unsigned)pushed);
+  repro::FoldSlotPtrs sl = {};
+  for (int L = 0; L <= t; ++L) {
+    if (slots[L] == nullptr) return REPRO_EINVAL;
+    if (!aligned4(slots[L])) return REPRO_EALIGN;
+    sl.p[L] = slots[L];
+  }
+  if (!aligned4(part)) return REPRO_EALIGN;
+  return status_of(repro::launch_fold_push(sl, t, part, n, static_cast<hipStream_t>(stream)));
+}
+
+int repro_fold_result(float* const* slots, int32_t pushed, int64_t n, float* out, int32_t divisor, void* stream) {
+  if (slots == nullptr || pushed < 1 || pushed > 127 || n < 0 || divisor < 0) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (out == nullptr) return REPRO_EINVAL;
+  repro::FoldSlotPtrs sl = {};
+  for (int L = 0; L < REPRO_FOLD_SLOTS; ++L) {
+    if (((pushed >> L) & 1) == 0) continue;
+    if (slots[L] == nullptr) return REPRO_EINVAL;
+    if (!aligned4(slots[L])) return REPRO_EALIGN;
+    sl.p[L] = slots[L];
+  }
+  if (!aligned4(out)) return REPRO_EALIGN;
+  const float r = divisor > 0 ? reciprocal(divisor) : 1.0f;
+  return status_of(repro::launch_fold_result(sl, pushed, divisor > 0, r, out, n, static_cast<hipStream_t>(stream)));
 }
 
 int repro_adamw_variant(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,

@@ -35,6 +35,7 @@ SOURCES = {
     # directly (otherwise each product is first copied out of an AGPR).
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "state_hash.hip": [],
+    "replay.hip": [],
 }
 
 

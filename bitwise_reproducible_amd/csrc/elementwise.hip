@@ -16,39 +16,11 @@
 #include <array>
 #include <utility>
 
+#include "device_ops.h"
 #include "internal.h"
 
 namespace repro {
 namespace {
-
-// One binary32 operation each (the hardware mode applies the flush rule).
-__device__ __forceinline__ float add_c(float a, float b) { return a + b; }
-__device__ __forceinline__ float sub_c(float a, float b) { return a - b; }
-__device__ __forceinline__ float mul_c(float a, float b) { return a * b; }
-__device__ __forceinline__ float div_c(float a, float b) { return a / b; }
-__device__ __forceinline__ float sqrt_c(float a) { return __builtin_sqrtf(a); }
-
-// Streaming 16-byte accesses that bypass cache retention (nontemporal).
-typedef float f4v __attribute__((ext_vector_type(4)));
-__device__ __forceinline__ float4 ld_nt(const float4* p) {
-  const f4v v = __builtin_nontemporal_load(reinterpret_cast<const f4v*>(p));
-  return make_float4(v.x, v.y, v.z, v.w);
-}
-__device__ __forceinline__ void st_nt(float4 v, float4* p) {
-  f4v u = {v.x, v.y, v.z, v.w};
-  __builtin_nontemporal_store(u, reinterpret_cast<f4v*>(p));
-}
-
-__device__ __forceinline__ float4 add4(float4 a, float4 b) {
-  return make_float4(add_c(a.x, b.x), add_c(a.y, b.y), add_c(a.z, b.z), add_c(a.w, b.w));
-}
-__device__ __forceinline__ float4 mul4s(float4 a, float s) {
-  return make_float4(mul_c(a.x, s), mul_c(a.y, s), mul_c(a.z, s), mul_c(a.w, s));
-}
-__device__ __forceinline__ float add_v(float a, float b) { return add_c(a, b); }
-__device__ __forceinline__ float4 add_v(float4 a, float4 b) { return add4(a, b); }
-__device__ __forceinline__ float mul_vs(float a, float s) { return mul_c(a, s); }
-__device__ __forceinline__ float4 mul_vs(float4 a, float s) { return mul4s(a, s); }
 
 // ---------------------------------------------------------------------------
 // TreeFold (Appendix A.1, Algorithm 2), unrolled at compile time for a fixed

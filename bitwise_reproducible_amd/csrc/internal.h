@@ -14,6 +14,17 @@ struct ReplicaPtrs {
   const float* p[REPRO_MAX_REPLICAS];
 };
 
+// Algorithm 1 replay: the N * accum gradient buffers in mesh order.
+struct ReplayPtrs {
+  const float* p[REPRO_MAX_REPLAY_BUFFERS];
+};
+
+// Streaming TreeFold: one device buffer per fold level.
+constexpr int kFoldSlots = REPRO_FOLD_SLOTS;
+struct FoldSlotPtrs {
+  float* p[kFoldSlots];
+};
+
 // Host-prepared AdamW scalars (binary32, computed under the contract).
 struct AdamwScalars {
   float lr, beta1, beta2, eps, wd;
@@ -26,6 +37,13 @@ hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* 
 hipError_t launch_adamw(float* state, const float* grad, int64_t n, const AdamwScalars& s, int variant,
                         hipStream_t stream);
 hipError_t launch_fp32_ops(int op, const float* a, const float* b, float* out, int64_t n, hipStream_t stream);
+
+// replay.hip
+hipError_t launch_replay(const ReplayPtrs& a, int nbuf, int dp_replicate, int dp_shard, int accum, float r_accum,
+                         float r_shard, float r_rep, int64_t n, float* out, hipStream_t stream);
+hipError_t launch_fold_push(const FoldSlotPtrs& sl, int t, const float* part, int64_t n, hipStream_t stream);
+hipError_t launch_fold_result(const FoldSlotPtrs& sl, int pushed, int average, float r, float* out, int64_t n,
+                              hipStream_t stream);
 
 // gemm.hip
 hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -56,6 +56,8 @@ extern "C" {
 #define REPRO_ESPACE -4 /* hash workspace too small */
 
 #define REPRO_MAX_REPLICAS 64
+#define REPRO_MAX_REPLAY_BUFFERS 384
+#define REPRO_FOLD_SLOTS 7
 
 /* "repro-spec-1": names the orders, the constants and the hash parameters
  * below.  A change to any of them changes this string. */
@@ -122,6 +124,48 @@ int repro_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float*
  * 2 16-byte vectors, 64 threads and a grid-stride loop over a small grid. */
 int repro_tree_reduce_variant(const float* const* replicas, int32_t R, int64_t n, float* out,
                               int32_t average, int32_t variant, void* stream);
+
+/*
+ * repro_replay_reduce: the audit replay of one step's gradient reduction.
+ *
+ * Paper section 6, Algorithm 1, with Appendix A.1 (TreeFold over replicas),
+ * A.2 (ascending-shard sum) and A.3 (every average a multiply by a
+ * host-computed reciprocal).  N = dp_replicate * dp_shard virtual ranks in
+ * mesh order r = rep * dp_shard + shard; rank r has `accum` microbatch
+ * gradients, grads[r * accum + k].  Per element:
+ *   g_r = +0, then g_r = g_r + grad[r][k] * fl(1/accum) for k = 0..accum-1;
+ *   inner = g_r for shard 0, inner = inner + g_r for shards 1..dp_shard-1;
+ *   at the replica's last shard: Push(inner * fl(1/dp_shard));
+ *   out = Result() * fl(1/dp_replicate)   (TreeFold as in repro_tree_reduce).
+ *
+ *   grads: HOST array of dp_replicate * dp_shard * accum device pointers,
+ *          each to n floats (at most REPRO_MAX_REPLAY_BUFFERS in all).
+ *   dp_replicate: 1..REPRO_MAX_REPLICAS; dp_shard, accum: >= 1.
+ *   out:   device pointer to n floats; may equal one of the buffers.
+ * n == 0: nothing to do.
+ */
+int repro_replay_reduce(const float* const* grads, int32_t dp_replicate, int32_t dp_shard, int32_t accum,
+                        int64_t n, float* out, void* stream);
+
+/*
+ * repro_fold_push / repro_fold_result: TreeFold (Appendix A.1, Algorithm 2)
+ * as a streaming interface for partials that arrive one at a time, holding
+ * at most floor(log2 R) + 1 partials ("at most 4" for R = 8).
+ *
+ *   slots:  HOST array of REPRO_FOLD_SLOTS device buffers of n floats, owned
+ *           by the caller; slots[L] holds the fold's entry of level L, which
+ *           exists exactly when bit L of `pushed` is set.  Only slots that
+ *           the call reads or writes need to be valid pointers.
+ *   pushed: the number of partials pushed before this call (the caller
+ *           counts); push accepts 0..126, result 1..127.
+ * repro_fold_push adds `part` to the occupied levels 0, 1, ... while their
+ * bits are set (the earlier, lower block on the left) and stores the sum in
+ * the first free level.  `part` may be that free slot.
+ * repro_fold_result writes the lowest occupied level plus the others in
+ * ascending level order to `out`, times fl(1/divisor) when divisor > 0.
+ */
+int repro_fold_push(float* const* slots, int32_t pushed, const float* part, int64_t n, void* stream);
+int repro_fold_result(float* const* slots, int32_t pushed, int64_t n, float* out, int32_t divisor, void* stream);
 
 /*
  * repro_adamw: one fused AdamW step, in place, on the flat binary32 state.
