@@ -18,6 +18,10 @@ it for its initialisation in section 3.1):
 * adamw   - n=1.2e9: w ~ N(0,0.02), m ~ N(0,1e-4), v = |N(0,1e-6)|,
             g ~ N(0,1e-3); step 1000, lr 3e-4, wd 0.1.
 * dw      - dW = X^T dY with X[16384x2048], dY[16384x8192], both 1e-2 * t(3).
+* replay  - the audit replay of one step's reduction at the OPEN-1B main-phase
+            layout: 6 replicas x 8 shards x 6 microbatches = 288 gradient
+            buffers of an n=8,388,608 slice, each N(0,1e-3) with 0.1% of
+            entries replaced by N(0,10).
 """
 from __future__ import annotations
 
@@ -97,6 +101,7 @@ REDUCE = dict(R=8, n=16_777_216)
 GEMM = dict(M=8192, N=8192, K=2048)
 ADAMW = dict(n=1_200_000_000, lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, wd=0.1, step=1000)
 DW = dict(M=2048, N=8192, K=16384)
+REPLAY = dict(dp_replicate=6, dp_shard=8, accum=6, n=8_388_608)
 
 
 def tiny_gemm_inputs(M=64, N=64, K=64):
@@ -155,3 +160,11 @@ def dw_x(rows=DW["K"], row0=0, out=None):
 def dw_dy(rows=DW["K"], row0=0, out=None):
     cols = DW["N"]
     return generate(rows * cols, STUDENT_T3, tid(5, 0x01), 1e-2, offset=row0 * cols, out=out)
+
+
+def replay_grad(b: int, n: int = REPLAY["n"], offset: int = 0, out=None):
+    """Microbatch gradient buffer b (mesh order, rank-major) of the replay workload.
+
+    Its 288 tensor ids sit above the one-byte index range of the other
+    workloads: 0x60000 + b."""
+    return generate(n, OUTLIER_REPLACE, (6 << 16) | b, 1e-3, 0.001, 10.0, offset=offset, out=out)
