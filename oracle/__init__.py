@@ -29,6 +29,8 @@ def _load():
         i64, vp, i32, f32 = ctypes.c_int64, ctypes.c_void_p, ctypes.c_int32, ctypes.c_float
         lib.oracle_fp32_ops.argtypes = [ctypes.c_int, vp, vp, vp, i64]
         lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.oracle_gemm_fma.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
+        lib.oracle_fma.argtypes = [vp, vp, vp, vp, i64]
         lib.oracle_tree_reduce.argtypes = [vp, i32, i64, vp, i32, vp]
         lib.oracle_replay_reduce.argtypes = [vp, i32, i32, i32, i64, vp]
         lib.oracle_fold_push.argtypes = [vp, i32, vp, i64]
@@ -99,8 +101,18 @@ def fp32_op(op: int, a, b=None) -> np.ndarray:
     return out
 
 
-def gemm(A, B, trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
-    """C = op(A) @ op(B) with one ascending-k unfused chain per output."""
+def fma(a, b, c) -> np.ndarray:
+    """fl(a*b + c) rounded once, under the contract's subnormal rule."""
+    a, b, c = _f32(a), _f32(b), _f32(c)
+    assert a.shape == b.shape == c.shape
+    out = np.empty_like(a)
+    _check(_load().oracle_fma(a.ctypes.data, b.ctypes.data, c.ctypes.data, out.ctypes.data, a.size), "fma")
+    return out
+
+
+def gemm(A, B, trans_a: bool = False, trans_b: bool = False, fused: bool = False) -> np.ndarray:
+    """C = op(A) @ op(B) with one ascending-k chain per output: unfused
+    multiply then add (the pages' convention), or fused when `fused`."""
     A = _f32(A)
     B = _f32(B)
     M, K = (A.shape[1], A.shape[0]) if trans_a else A.shape
@@ -109,8 +121,9 @@ def gemm(A, B, trans_a: bool = False, trans_b: bool = False) -> np.ndarray:
     C = np.empty((M, N), dtype=np.float32)
     lda = A.shape[1] if A.ndim == 2 and A.shape[1] > 0 else 1
     ldb = B.shape[1] if B.ndim == 2 and B.shape[1] > 0 else 1
-    _check(_load().oracle_gemm(int(trans_a), int(trans_b), M, N, K, A.ctypes.data, lda, B.ctypes.data,
-                               ldb, C.ctypes.data, max(N, 1)), "gemm")
+    fn = _load().oracle_gemm_fma if fused else _load().oracle_gemm
+    _check(fn(int(trans_a), int(trans_b), M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, C.ctypes.data,
+              max(N, 1)), "gemm")
     return C
 
 

@@ -19,6 +19,8 @@
  * The checkpoint page ("grow a language model: checkpoints", section on the
  * file format) fixes the flat [w | m | v] order and beta2 = 0.999.
  * BLAKE2b itself follows RFC 7693 (Saarinen and Aumasson, 2015).
+ * One declared alternative the pages do not use: a fused multiply-add GEMM
+ * convention (oracle_fma, oracle_gemm_fma), for matrix-core chains.
  *
  * Floating-point model.  Section 2.1 has the processor path flush subnormals
  * by turning on its FTZ and DAZ modes.  On this x86-64 host those are the
@@ -105,6 +107,97 @@ int oracle_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
                 float a = trans_a ? A[k * lda + i] : A[i * lda + k];
                 float b = trans_b ? B[j * ldb + k] : B[k * ldb + j];
                 acc = f_add(acc, f_mul(a, b));
+            }
+            C[i * ldc + j] = acc;
+        }
+    }
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* The fused multiply-add convention (a declared alternative: the pages keep
+ * multiply and add unfused, section 2.1 "Fused multiply-add").
+ *
+ * fma(a, b, c) = fl(a*b + c), one rounding, under the same subnormal rule as
+ * every other operation: a subnormal a, b or c reads as a zero of the same
+ * sign; the exact a*b + c is rounded to 24 significant bits with an
+ * unbounded exponent, and a result whose magnitude is then below 2^-126
+ * becomes a zero of the same sign.
+ *
+ * Written from that definition without any fused instruction: a*b is exact
+ * in binary64 (two 24-bit significands make at most 48 bits), the sum is
+ * rounded to odd in binary64, and rounding that to 24 bits gives the
+ * correctly rounded a*b + c (Boldo and Melquiond, "Emulation of FMA and
+ * correctly rounded sums: proved algorithms using rounding to odd", IEEE
+ * Trans. Computers 57(4), 2008: the odd rounding at p + 2 or more bits
+ * followed by a nearest rounding at p bits equals one nearest rounding).
+ * All binary64 values involved are normal, so the SSE flush modes leave
+ * them alone.  (The operands are read as zeros explicitly; under DAZ the
+ * conversion to binary64 would do the same.) */
+static float f_daz(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    if ((u & 0x7F800000u) == 0) u &= 0x80000000u;
+    memcpy(&x, &u, 4);
+    return x;
+}
+
+static double sum_round_to_odd(double p, double c) {
+    double s = p + c;                            /* nearest */
+    double bp = s - p;
+    double err = (p - (s - bp)) + (c - bp);      /* p + c - s exactly (Knuth's TwoSum) */
+    if (err != 0.0) {
+        uint64_t bits;
+        memcpy(&bits, &s, 8);
+        if ((bits & 1u) == 0) s = nextafter(s, err > 0.0 ? INFINITY : -INFINITY);
+    }
+    return s;
+}
+
+static float f_fma(float a, float b, float c) {
+    a = f_daz(a);
+    b = f_daz(b);
+    c = f_daz(c);
+    const double s = sum_round_to_odd((double)a * (double)b, (double)c);
+    if (s == 0.0) return (float)s;
+    /* Round to 24 bits with an unbounded exponent: move tiny values into the
+     * normal binary32 range by an exact power-of-two scaling first. */
+    double r24;
+    if (fabs(s) < 0x1p-64) r24 = (double)(float)(s * 0x1p+128) * 0x1p-128;
+    else r24 = (double)(float)s;
+    if (fabs(r24) < 0x1p-126) return s < 0.0 ? -0.0f : 0.0f;
+    return (float)r24;
+}
+
+/* Elementwise fma under the contract, exported for the directed tests. */
+int oracle_fma(const float* a, const float* b, const float* c, float* out, int64_t n) {
+    if (n < 0) return ORACLE_EINVAL;
+    fpenv_t e = enter_contract();
+    for (int64_t i = 0; i < n; ++i) out[i] = f_fma(a[i], b[i], c[i]);
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* GEMM under the fused convention: the same chains in the same order as
+ * oracle_gemm, each step acc <- fma(a_ik, b_kj, acc), starting from +0. */
+int oracle_gemm_fma(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K,
+                    const float* A, int64_t lda, const float* B, int64_t ldb,
+                    float* C, int64_t ldc) {
+    if (M < 0 || N < 0 || K < 0) return ORACLE_EINVAL;
+    if (M == 0 || N == 0) return ORACLE_OK;
+    if (ldc < N) return ORACLE_EINVAL;
+    if (K > 0) {
+        if (lda < (trans_a ? M : K) || ldb < (trans_b ? K : N)) return ORACLE_EINVAL;
+    }
+    fpenv_t e = enter_contract();
+    for (int64_t i = 0; i < M; ++i) {
+        for (int64_t j = 0; j < N; ++j) {
+            float acc = 0.0f;
+            for (int64_t k = 0; k < K; ++k) {
+                float a = trans_a ? A[k * lda + i] : A[i * lda + k];
+                float b = trans_b ? B[j * ldb + k] : B[k * ldb + j];
+                acc = f_fma(a, b, acc);
             }
             C[i * ldc + j] = acc;
         }

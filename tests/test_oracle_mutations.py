@@ -13,6 +13,7 @@ import oracle
 from oracle import build as oracle_build
 
 import test_oracle_adamw as T_ADAMW
+import test_oracle_fma as T_FMA
 import test_oracle_fp32 as T_FP32
 import test_oracle_gemm as T_GEMM
 import test_oracle_hash as T_HASH
@@ -66,6 +67,13 @@ MUTATIONS = [
      [lambda: T_HASH.test_tree_mode_matches_hashlib(1025)]),
     ("blake2b_rotation", "v[b] = rotr64(v[b] ^ v[c], 63);", "v[b] = rotr64(v[b] ^ v[c], 62);",
      [T_HASH.test_rfc7693_known_answer]),
+    ("fma_double_rounding", "const double s = sum_round_to_odd((double)a * (double)b, (double)c);",
+     "const double s = (double)a * (double)b + (double)c;",
+     [lambda: T_FMA.test_no_double_rounding(1)]),
+    ("fma_flush_before_rounding", "if (fabs(r24) < 0x1p-126)", "if (fabs(s) < 0x1p-126)",
+     [T_FMA.test_flush_after_rounding_to_24_bits]),
+    ("gemm_fma_unfused", "acc = f_fma(a, b, acc);", "acc = f_add(acc, f_mul(a, b));",
+     [T_FMA.test_fused_witness]),
     ("no_flush", "_mm_setcsr((e.saved & ~0x6000u) | 0x8000u | 0x0040u | 0x1F80u);",
      "_mm_setcsr((e.saved & ~(0x6000u | 0x8000u | 0x0040u)) | 0x1F80u);",
      [T_FP32.test_subnormal_results_flush_with_sign, T_FP32.test_subnormal_operands_read_as_signed_zero]),
