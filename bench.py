@@ -11,8 +11,9 @@ every input already resident in HBM:
 Each op is bracketed by HIP events on the stream it runs on.  After the
 steps, the audit replay of one step's reduction (OPEN-1B section 6,
 Algorithm 1: 6 replicas x 8 shards x 6 microbatches over an 8,388,608-float
-slice, repro_replay_reduce) is timed on its own and reported under
-"next_rows"; it is not part of the step.  `value` is the
+slice, repro_replay_reduce) and the fused multiply-add GEMM convention
+(repro_gemm_fma on both GEMM workloads, matrix cores and VALU) are timed on
+their own and reported under "next_rows"; they are not part of the step.  `value` is the
 GB/s of the memory-side ops (1, 3, 4: algorithmic bytes over their summed
 event time); the GEMMs are reported in GFLOP/s beside it.  After the timed
 steps the outputs are checked against the CPU oracle (every word of the
@@ -238,6 +239,26 @@ def main():
     torch.cuda.synchronize()
     replay_ms = float(np.mean([p_evs[s].elapsed_time(p_evs[s + 1]) for s in range(args.steps)]))
 
+    # The fused multiply-add GEMM convention (declared alternative), both
+    # workloads, matrix cores (variant 0) and VALU (variant 1).
+    Y3f = torch.empty_like(Y3)
+    dW5f = torch.empty_like(dW5)
+    fma_ms = {}
+    for variant in (0, 1):
+        for name, call in (("fwd", lambda v: br.repro_gemm_fma(X3, W3, out=Y3f, variant=v)),
+                           ("dw", lambda v: br.repro_gemm_fma(X5, dY5, trans_a=True, out=dW5f, variant=v))):
+            for _ in range(args.warmup):
+                call(variant)
+            f_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+            torch.cuda.synchronize()
+            f_evs[0].record()
+            for s_ in range(args.steps):
+                call(variant)
+                f_evs[s_ + 1].record()
+            torch.cuda.synchronize()
+            fma_ms[(variant, name)] = float(np.mean([f_evs[i].elapsed_time(f_evs[i + 1])
+                                                     for i in range(args.steps)]))
+
     if args.calibration_copy:
         br.repro_tree_reduce([reps[0]], out=g_red, average=False)
         torch.cuda.synchronize()
@@ -283,6 +304,14 @@ def main():
                     f"({p_nbuf} buffers) n={PC['n']}",
         "ms": round(replay_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce")}}
+    for variant, unit in ((0, "matrix cores, v_mfma_f32_32x32x1_2b_f32"), (1, "VALU, v_fma_f32")):
+        ms = fma_ms[(variant, "fwd")] + fma_ms[(variant, "dw")]
+        ach = (flops_fwd + flops_dw) / (ms * 1e-3) / 1e12
+        next_rows[f"gemm_fma_variant{variant}"] = {
+            "workload": "fused-MAC chains: gemm 8192x2048 @ 2048x8192 and dW 2048x8192 K=16384", "unit": unit,
+            "ms_fwd": round(fma_ms[(variant, "fwd")], 4), "ms_dw": round(fma_ms[(variant, "dw")], 4),
+            "bound": "mfma" if variant == 0 else "alu", "achieved": round(ach, 3), "peak": FP32_VECTOR_PEAK,
+            "unit_rate": "TFLOP/s", "frac": round(ach / FP32_VECTOR_PEAK, 4)}
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
@@ -300,6 +329,7 @@ def main():
         out["verified"] = verify(torch, np, br, reps, g_red, X3, W3, Y3, X5, dY5, dW5, state, ws, n, aidx,
                                  (s_w, s_m, s_v, s_g), hp, AC["step"], args.warmup + args.steps)
         out["verified"].update(verify_replay(np, p_out, p_layout, PC["n"]))
+        out["verified"].update(verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np)
     print(json.dumps(out), flush=True)
@@ -378,6 +408,29 @@ def verify_replay(np, p_out, layout, n):
         bad += int(np.count_nonzero(got.view(np.uint32) != ref.view(np.uint32)))
     return {"replay_sampled_words_differing": bad, "replay_sampled_words": len(starts) * m,
             "replay_seconds": round(time.time() - t, 1)}
+
+
+def verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f):
+    """The last fused GEMM outputs (VALU variant) against the oracle's fused
+    chains on sampled rows and columns."""
+    import oracle
+    t = time.time()
+    bad = 0
+    x3 = X3.cpu().numpy()
+    bt3 = np.ascontiguousarray(W3.cpu().numpy().T)
+    y = Y3f.cpu().numpy()
+    bad += int(np.count_nonzero(y[4097].view(np.uint32) !=
+                                oracle.gemm(x3[4097:4098], bt3, trans_b=True, fused=True)[0].view(np.uint32)))
+    bad += int(np.count_nonzero(y[:, 8191].view(np.uint32) !=
+                                oracle.gemm(x3, bt3[8191:], trans_b=True, fused=True)[:, 0].view(np.uint32)))
+    a5 = np.ascontiguousarray(X5.cpu().numpy().T)
+    bt5 = np.ascontiguousarray(dY5.cpu().numpy().T)
+    g = dW5f.cpu().numpy()
+    bad += int(np.count_nonzero(g[1029].view(np.uint32) !=
+                                oracle.gemm(a5[1029:1030], bt5, trans_b=True, fused=True)[0].view(np.uint32)))
+    bad += int(np.count_nonzero(g[:, 77].view(np.uint32) !=
+                                oracle.gemm(a5, bt5[77:78], trans_b=True, fused=True)[:, 0].view(np.uint32)))
+    return {"gemm_fma_sampled_words_differing": bad, "gemm_fma_seconds": round(time.time() - t, 1)}
 
 
 def cpu_baseline(np):

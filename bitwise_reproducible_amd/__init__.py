@@ -7,13 +7,14 @@ HIP kernels; there is no fallback, and a missing library is an error.
 
 Entry points (same names as the C ABI):
     repro_gemm(A, B, trans_a=False, trans_b=False, out=None)
+    repro_gemm_fma(A, B, trans_a=False, trans_b=False, out=None, variant=0)
     repro_tree_reduce(replicas, out=None, average=True)
     repro_replay_reduce(grads, dp_replicate, dp_shard, accum, out=None)
     repro_fold_push(slots, pushed, part);  repro_fold_result(slots, pushed, out, divisor=0)
     repro_adamw(state, grad, lr, beta1, beta2, eps, weight_decay, step)
     repro_state_hash(words, workspace=None) -> 32-byte digest (bytes)
     repro_state_hash_async(words, digest_out, workspace)
-    repro_fp32_ops(op, a, b, out=None)
+    repro_fp32_ops(op, a, b, out=None);  repro_fp32_fma(a, b, c, unit=0, out=None)
 """
 from __future__ import annotations
 
@@ -63,9 +64,12 @@ def library():
         lib.repro_replay_reduce.argtypes = [vp, i32, i32, i32, i64, vp, vp]
         lib.repro_fold_push.argtypes = [vp, i32, vp, i64, vp]
         lib.repro_fold_result.argtypes = [vp, i32, i64, vp, i32, vp]
+        lib.repro_gemm_fma.argtypes = gemm_args + [i32, vp]
+        lib.repro_fp32_fma.argtypes = [vp, vp, vp, vp, i64, i32, vp]
         for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
                      "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops",
-                     "repro_replay_reduce", "repro_fold_push", "repro_fold_result"):
+                     "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_gemm_fma",
+                     "repro_fp32_fma"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -109,8 +113,10 @@ def _row_major(t, name: str):
     return t.data_ptr(), rows, cols, max(ld, cols, 1)
 
 
-def repro_gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, variant: int = 0, stream=None):
-    """C = op(A) @ op(B), one ascending-k unfused chain per output."""
+def repro_gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, variant: int = 0, stream=None,
+               fused: bool = False):
+    """C = op(A) @ op(B), one ascending-k unfused chain per output (fused: the
+    declared fused multiply-add chain of repro_gemm_fma)."""
     import torch
     pa, ra, ca, lda = _row_major(A, "A")
     pb, rb, cb, ldb = _row_major(B, "B")
@@ -124,13 +130,21 @@ def repro_gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, var
     if (rc, cc) != (M, N):
         raise ValueError("out has the wrong shape")
     lib = library()
-    if variant == 0:
+    if fused:
+        st = lib.repro_gemm_fma(int(trans_a), int(trans_b), M, N, K, pa, lda, pb, ldb, pc, ldc, int(variant),
+                                _stream(stream))
+    elif variant == 0:
         st = lib.repro_gemm(int(trans_a), int(trans_b), M, N, K, pa, lda, pb, ldb, pc, ldc, _stream(stream))
     else:
         st = lib.repro_gemm_variant(int(trans_a), int(trans_b), M, N, K, pa, lda, pb, ldb, pc, ldc, int(variant),
                                     _stream(stream))
-    _check(st, "repro_gemm")
+    _check(st, "repro_gemm_fma" if fused else "repro_gemm")
     return out
+
+
+def repro_gemm_fma(A, B, trans_a: bool = False, trans_b: bool = False, out=None, variant: int = 0, stream=None):
+    """C = op(A) @ op(B) under the fused convention (0: matrix cores, 1: VALU)."""
+    return repro_gemm(A, B, trans_a, trans_b, out, variant, stream, fused=True)
 
 
 def repro_tree_reduce(replicas, out=None, average: bool = True, variant: int = 0, stream=None):
@@ -275,6 +289,21 @@ def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
     return out
 
 
-__all__ = ["repro_gemm", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
+def repro_fp32_fma(a, b, c, unit: int = 0, out=None, stream=None):
+    """out = fma(a, b, c) per element on one unit (0: v_fma_f32, 1: matrix core)."""
+    import torch
+    for t, nm in ((a, "a"), (b, "b"), (c, "c")):
+        _f32_device(t, nm)
+    if out is None:
+        out = torch.empty_like(a)
+    ts = (a, b, c, out)
+    if not all(t.is_contiguous() for t in ts) or len({t.numel() for t in ts}) != 1:
+        raise ValueError("a, b, c, out must be contiguous and of equal size")
+    _check(library().repro_fp32_fma(a.data_ptr(), b.data_ptr(), c.data_ptr(), out.data_ptr(), a.numel(), int(unit),
+                                    _stream(stream)), "repro_fp32_fma")
+    return out
+
+
+__all__ = ["repro_gemm", "repro_gemm_fma", "repro_fp32_fma", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
            "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
            "ReproError", "LIB_PATH"]

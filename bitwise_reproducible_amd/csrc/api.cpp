@@ -84,9 +84,11 @@ const char* repro_strerror(int status) {
   }
 }
 
-int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                       const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream) {
-  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > 3) return REPRO_EINVAL;
+namespace {
+
+int gemm_checked(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                 const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, bool fused, void* stream) {
+  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > (fused ? 1 : 3)) return REPRO_EINVAL;
   if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return REPRO_EINVAL;
   if (M == 0 || N == 0) return REPRO_OK;
   if (C == nullptr || ldc < N) return REPRO_EINVAL;
@@ -96,8 +98,20 @@ int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
     if (!aligned4(A) || !aligned4(B)) return REPRO_EALIGN;
   }
   if (!aligned4(C)) return REPRO_EALIGN;
-  return status_of(repro::launch_gemm(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, variant,
+  return status_of(repro::launch_gemm(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, variant, fused,
                                       static_cast<hipStream_t>(stream)));
+}
+
+}  // namespace
+
+int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream) {
+  return gemm_checked(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, variant, false, stream);
+}
+
+int repro_gemm_fma(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                   const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream) {
+  return gemm_checked(trans_a, trans_b, M, N, K, A, lda, B, ldb, C, ldc, variant, true, stream);
 }
 
 int repro_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
@@ -222,6 +236,15 @@ int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64
   if (a == nullptr || b == nullptr || out == nullptr) return REPRO_EINVAL;
   if (!aligned4(a) || !aligned4(b) || !aligned4(out)) return REPRO_EALIGN;
   return status_of(repro::launch_fp32_ops(op, a, b, out, n, static_cast<hipStream_t>(stream)));
+}
+
+int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
+                   void* stream) {
+  if (unit < 0 || unit > 1 || n < 0) return REPRO_EINVAL;
+  if (n == 0) return REPRO_OK;
+  if (a == nullptr || b == nullptr || c == nullptr || out == nullptr) return REPRO_EINVAL;
+  if (!aligned4(a) || !aligned4(b) || !aligned4(c) || !aligned4(out)) return REPRO_EALIGN;
+  return status_of(repro::launch_fp32_fma(unit, a, b, c, out, n, static_cast<hipStream_t>(stream)));
 }
 
 }  // extern "C"

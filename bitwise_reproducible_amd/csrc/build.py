@@ -36,6 +36,7 @@ SOURCES = {
     "gemm.hip": ["-mllvm", "-amdgpu-mfma-vgpr-form"],
     "state_hash.hip": [],
     "replay.hip": [],
+    "fused.hip": [],
 }
 
 

@@ -66,10 +66,10 @@ __device__ __forceinline__ float4 load_chunk(const float* __restrict__ p, int64_
   return v;
 }
 
-template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
-__global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
-    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
-    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC, bool FUSED>
+__device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
+                                          int64_t lda, const float* __restrict__ B, int64_t ldb,
+                                          float* __restrict__ C, int64_t ldc, int tiles_n) {
   using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
   __shared__ __attribute__((aligned(16))) float As[2][BK][BM + T::PAD];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + T::PAD];
@@ -147,7 +147,8 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;  // the chain starts at +0
 
-  // One k step: every output of the lane takes fl(acc + fl(a * b)).
+  // One k step: every output of the lane takes fl(acc + fl(a * b)), or
+  // fl(a * b + acc) rounded once under the fused convention.
   auto mac_step = [&](int buf, int kk) {
     float a[TM], b[TN];
 #pragma unroll
@@ -162,8 +163,12 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
-        const float p = a[i] * b[j];
-        acc[i][j] = acc[i][j] + p;
+        if constexpr (FUSED) {
+          acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+        } else {
+          const float p = a[i] * b[j];
+          acc[i][j] = acc[i][j] + p;
+        }
       }
   };
 
@@ -211,6 +216,21 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
     }
 }
 
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
+  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+}
+
+// The fused convention on the VALU: one v_fma_f32 per step of each chain.
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm_fma(
+    int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
+  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+}
+
 // ---------------------------------------------------------------------------
 // Matrix-core multiply, VALU add.
 //
@@ -237,10 +257,10 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
 // staged through LDS exactly as in the VALU kernel.
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
-template <int BK, bool TA, bool TB, bool VEC>
-__global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
-                                                   int64_t lda, const float* __restrict__ B, int64_t ldb,
-                                                   float* __restrict__ C, int64_t ldc, int tiles_n) {
+template <int BK, bool TA, bool TB, bool VEC, bool FUSED>
+__device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
+                                               int64_t lda, const float* __restrict__ B, int64_t ldb,
+                                               float* __restrict__ C, int64_t ldc, int tiles_n) {
   constexpr int BM = 128, BN = 128, NT = 256, PAD = 4;
   constexpr int LA = BM * BK / 4 / NT, LB = BK * BN / 4 / NT;
   static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
@@ -323,12 +343,18 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t
     const float a = As[buf][kk][wm + lane];
     const float b0 = Bs[buf][kk][wn + (lane & 31)];
     const float b1 = Bs[buf][kk][wn + 32 + (lane & 31)];
-    const floatx32 p0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, negz, 0, 0, 0);
-    const floatx32 p1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b1, negz, 0, 0, 0);
+    if constexpr (FUSED) {
+      // The chain value is the C operand: acc = fl(a * b + acc), one rounding.
+      acc0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, acc0, 0, 0, 0);
+      acc1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b1, acc1, 0, 0, 0);
+    } else {
+      const floatx32 p0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, negz, 0, 0, 0);
+      const floatx32 p1 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b1, negz, 0, 0, 0);
 #pragma unroll
-    for (int r = 0; r < 32; ++r) acc0[r] = acc0[r] + p0[r];
+      for (int r = 0; r < 32; ++r) acc0[r] = acc0[r] + p0[r];
 #pragma unroll
-    for (int r = 0; r < 32; ++r) acc1[r] = acc1[r] + p1[r];
+      for (int r = 0; r < 32; ++r) acc1[r] = acc1[r] + p1[r];
+    }
   };
 
   const int64_t nslabs = (K + BK - 1) / BK;
@@ -366,23 +392,47 @@ __global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t
 }
 
 template <int BK, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
+                                                   int64_t lda, const float* __restrict__ B, int64_t ldb,
+                                                   float* __restrict__ C, int64_t ldc, int tiles_n) {
+  gemm_mfma_tile<BK, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+}
+
+// The fused convention on the matrix cores: v_mfma_f32_32x32x1_2b_f32 with
+// K = 1 and the chain as C is one fused multiply-add per output per step, so
+// consecutive instructions over ascending k form exactly the serial fused
+// chain of every output, with no VALU arithmetic at all.
+template <int BK, bool TA, bool TB, bool VEC>
+__global__ __launch_bounds__(256) void k_gemm_mfma_fma(int64_t M, int64_t N, int64_t K,
+                                                       const float* __restrict__ A, int64_t lda,
+                                                       const float* __restrict__ B, int64_t ldb,
+                                                       float* __restrict__ C, int64_t ldc, int tiles_n) {
+  gemm_mfma_tile<BK, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+}
+
+template <int BK, bool TA, bool TB, bool VEC, bool FUSED>
 hipError_t launch_mfma(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B, int64_t ldb,
                        float* C, int64_t ldc, hipStream_t stream) {
   const int64_t tiles_m = (M + 127) / 128;
   const int64_t tiles_n = (N + 127) / 128;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm_mfma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A, lda,
-                     B, ldb, C, ldc, (int)tiles_n);
+  if constexpr (FUSED)
+    hipLaunchKernelGGL((k_gemm_mfma_fma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A,
+                       lda, B, ldb, C, ldc, (int)tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm_mfma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A,
+                       lda, B, ldb, C, ldc, (int)tiles_n);
   return hipGetLastError();
 }
 
+template <bool FUSED>
 hipError_t dispatch_mfma(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                          const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
-#define REPRO_GEMM_CASE(TA_, TB_)                                                                 \
-  if (ta == TA_ && tb == TB_)                                                                     \
-    return vec ? launch_mfma<16, TA_, TB_, true>(M, N, K, A, lda, B, ldb, C, ldc, stream)         \
-               : launch_mfma<16, TA_, TB_, false>(M, N, K, A, lda, B, ldb, C, ldc, stream);
+#define REPRO_GEMM_CASE(TA_, TB_)                                                                     \
+  if (ta == TA_ && tb == TB_)                                                                         \
+    return vec ? launch_mfma<16, TA_, TB_, true, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream)      \
+               : launch_mfma<16, TA_, TB_, false, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream);
   REPRO_GEMM_CASE(0, 0)
   REPRO_GEMM_CASE(1, 0)
   REPRO_GEMM_CASE(0, 1)
@@ -391,7 +441,7 @@ hipError_t dispatch_mfma(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t
   return hipErrorInvalidValue;
 }
 
-template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC, bool FUSED>
 hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t lda, const float* B,
                         int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
   using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
@@ -399,18 +449,24 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL((k_gemm<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
-                     M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
+  if constexpr (FUSED)
+    hipLaunchKernelGGL((k_gemm_fma<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0,
+                       stream, M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
+  else
+    hipLaunchKernelGGL((k_gemm<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
+                       M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
   return hipGetLastError();
 }
 
-template <int BM, int BN, int BK, int TM, int TN>
+template <int BM, int BN, int BK, int TM, int TN, bool FUSED>
 hipError_t dispatch(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                     const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
-#define REPRO_GEMM_CASE(TA_, TB_)                                                                          \
-  if (ta == TA_ && tb == TB_)                                                                              \
-    return vec ? launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, true>(M, N, K, A, lda, B, ldb, C, ldc, stream) \
-               : launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, false>(M, N, K, A, lda, B, ldb, C, ldc, stream);
+#define REPRO_GEMM_CASE(TA_, TB_)                                                                             \
+  if (ta == TA_ && tb == TB_)                                                                                 \
+    return vec ? launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, true, FUSED>(M, N, K, A, lda, B, ldb, C, ldc,     \
+                                                                         stream)                              \
+               : launch_tiled<BM, BN, BK, TM, TN, TA_, TB_, false, FUSED>(M, N, K, A, lda, B, ldb, C, ldc,    \
+                                                                          stream);
   REPRO_GEMM_CASE(0, 0)
   REPRO_GEMM_CASE(1, 0)
   REPRO_GEMM_CASE(0, 1)
@@ -422,7 +478,8 @@ hipError_t dispatch(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, c
 }  // namespace
 
 hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, hipStream_t stream) {
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, bool fused,
+                       hipStream_t stream) {
   auto al16 = [](const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; };
   // 16-byte loads need aligned bases, leading dimensions that keep rows
   // aligned, and a contiguous extent that is a multiple of 4 so that a
@@ -431,9 +488,15 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   const int64_t b_contig = trans_b ? K : N;
   const bool vec = variant != 1 && al16(A) && al16(B) && lda % 4 == 0 && ldb % 4 == 0 && a_contig % 4 == 0 &&
                    b_contig % 4 == 0;
-  if (variant == 2) return dispatch<64, 64, 16, 4, 4>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  if (variant == 3) return dispatch_mfma(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  return dispatch<128, 128, 16, 8, 8>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  if (fused) {  // variant 0: matrix cores, 1: VALU v_fma_f32
+    if (variant == 0)
+      return dispatch_mfma<true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return dispatch<128, 128, 16, 8, 8, true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  }
+  if (variant == 2)
+    return dispatch<64, 64, 16, 4, 4, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  if (variant == 3) return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  return dispatch<128, 128, 16, 8, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 }  // namespace repro

@@ -47,7 +47,12 @@ hipError_t launch_fold_result(const FoldSlotPtrs& sl, int pushed, int average, f
 
 // gemm.hip
 hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
-                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, hipStream_t stream);
+                       const float* B, int64_t ldb, float* C, int64_t ldc, int variant, bool fused,
+                       hipStream_t stream);
+
+// fused.hip
+hipError_t launch_fp32_fma(int unit, const float* a, const float* b, const float* c, float* out, int64_t n,
+                           hipStream_t stream);
 
 // state_hash.hip
 struct HashPlan {

@@ -96,6 +96,29 @@ int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
                        void* stream);
 
 /*
+ * repro_gemm_fma: the same GEMM under a declared fused multiply-add
+ * convention, which the pages do not use (paper section 2.1 "Fused
+ * multiply-add" keeps multiply and add unfused on every backend).  It is
+ * for callers that declare this convention for their whole run; its results
+ * differ from repro_gemm's.
+ *
+ * Each C[i][j] is one serial chain over k = 0, 1, ..., K-1 ascending:
+ * acc = +0, then acc = fma(opA[i][k], opB[k][j], acc), where fma(a, b, c) is
+ * a*b + c rounded once to binary32 (nearest-even) under the contract's
+ * subnormal rule: subnormal operands read as zeros of the same sign, and a
+ * result below 2^-126 after rounding to 24 bits (unbounded exponent) becomes
+ * a zero of the same sign.  Arguments, layout and errors as repro_gemm.
+ *
+ *   variant 0: matrix cores.  v_mfma_f32_32x32x1_2b_f32 with K = 1 takes the
+ *              chain value as its C operand, which is exactly one fused step
+ *              per output; consecutive instructions walk k in order.
+ *   variant 1: VALU, one v_fma_f32 per step (128x128 tile).
+ * Both variants return the same bits.
+ */
+int repro_gemm_fma(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
+                   const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, void* stream);
+
+/*
  * repro_tree_reduce: out[i] = Fold(x_0[i], ..., x_{R-1}[i]) (times fl(1/R)).
  *
  * Paper Appendix A.1 with Algorithm 2: TreeFold, the binary-carry fold that
@@ -232,6 +255,18 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
  * a, b, out: device pointers to n floats.
  */
 int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64_t n, void* stream);
+
+/*
+ * repro_fp32_fma: out[i] = fma(a[i], b[i], c[i]) under the fused convention
+ * of repro_gemm_fma, on one chosen unit: 0 = VALU v_fma_f32, 1 = the matrix
+ * core instruction v_mfma_f32_32x32x1_2b_f32 (each element placed on the
+ * diagonal of a 32x32 block, with c[i] as the C operand).  For directed
+ * tests of the single step each fused GEMM variant repeats.  Device pointers
+ * of n floats; out may equal a, b or c only if it equals all the inputs it
+ * overlaps element for element.
+ */
+int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
+                   void* stream);
 
 #ifdef __cplusplus
 }

@@ -1,0 +1,182 @@
+"""GPU parity for the declared fused multiply-add convention.
+
+The pages keep multiply and add unfused (OPEN-1B paper, section 2.1 "Fused
+multiply-add"); repro_gemm_fma declares the fused chain instead:
+acc = fma(a, b, acc), k ascending, one rounding per step, under the same
+subnormal rule.  Before any GEMM is trusted, each unit's single step is
+compared with the oracle's fma on directed operand sets:
+  unit 0 - VALU v_fma_f32
+  unit 1 - v_mfma_f32_32x32x1_2b_f32 with the chain value as C (K = 1)
+"""
+import numpy as np
+import pytest
+import torch
+
+import bitwise_reproducible_amd as br
+import oracle
+import synth
+from parity_util import assert_bitwise, to_dev, to_host
+
+pytestmark = pytest.mark.gpu
+
+UNITS = [0, 1]
+
+
+def _triples(seed, n):
+    rng = np.random.default_rng(seed)
+
+    def rnd(lo, hi):
+        m = rng.uniform(1, 2, n) * rng.choice([-1, 1], n)
+        return (m * 2.0 ** rng.integers(lo, hi, n)).astype(np.float32)
+
+    sets = []
+    # Random exponents, with c near -a*b for a third (cancellation).
+    a, b, c = rnd(-70, 60), rnd(-70, 60), rnd(-140, 120)
+    k = n // 3
+    c[:k] = (-(a[:k].astype(np.float64) * b[:k]) * (1 + rng.normal(0, 1e-6, k))).astype(np.float32)
+    sets.append((a, b, c))
+    # Products and sums around 2^-126, c of both signs, subnormal c.
+    a = (rng.uniform(1, 2, n) * 2.0 ** -63).astype(np.float32)
+    b = (rng.uniform(0.5, 1, n) * 2.0 ** -63).astype(np.float32)
+    c = (rng.choice([-1, 1], n) * rng.uniform(0, 2, n) * 2.0 ** -126).astype(np.float32)
+    c[::5] = (rng.uniform(0, 1, c[::5].size) * 2.0 ** -126).astype(np.float32)  # includes subnormals
+    sets.append((a, b, c))
+    # Subnormal multiplicands.
+    a = rnd(-150, -120)
+    b = rnd(-10, 10)
+    c = rnd(-130, -100)
+    sets.append((a, b, c))
+    # Exact ties after one rounding, and the double-rounding family
+    # a*b + c = 1 + 2^-24 + k^2 2^-70.
+    kk = rng.integers(1, 4000, n)
+    a = (1 + kk * 2.0 ** -23).astype(np.float32)
+    b = (-(2.0 ** -24) * (1 - kk * 2.0 ** -23)).astype(np.float32)
+    c = np.full(n, 1 + 2.0 ** -23, np.float32)
+    sets.append((a, b, c))
+    # Signed zeros and exact cancellation.
+    z = np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -126, -(2.0 ** -126)], np.float32)
+    g = np.array(np.meshgrid(z, z, z)).reshape(3, -1).astype(np.float32)
+    sets.append((g[0], g[1], g[2]))
+    return [tuple(np.ascontiguousarray(x) for x in s) for s in sets]
+
+
+@pytest.mark.parametrize("unit", UNITS)
+def test_single_step_matches_oracle(unit):
+    for si, (a, b, c) in enumerate(_triples(100 + unit, 200_003)):
+        ref = oracle.fma(a, b, c)
+        got = to_host(br.repro_fp32_fma(to_dev(a), to_dev(b), to_dev(c), unit=unit))
+        assert_bitwise(got, ref, f"unit {unit} set {si}")
+
+
+@pytest.mark.parametrize("n", [1, 63, 64, 65, 130, 4097])
+def test_mfma_unit_ragged_groups(n):
+    a, b, c = (synth.generate(n, synth.NORMAL, 0x9100 + i, 1.0) for i in range(3))
+    out = torch.full((n + 64,), 7.0, device="cuda")
+    br.repro_fp32_fma(to_dev(a), to_dev(b), to_dev(c), unit=1, out=out[:n])
+    assert_bitwise(to_host(out[:n]), oracle.fma(a, b, c), f"n={n}")
+    assert (to_host(out[n:]) == 7.0).all()  # nothing past the end was written
+
+
+def _mat(rows, cols, tid, std=1.0):
+    return synth.generate(rows * cols, synth.NORMAL, tid, std).reshape(rows, cols)
+
+
+SHAPES = [(1, 1, 1), (64, 64, 64), (200, 130, 77), (129, 257, 33), (3, 700, 5), (130, 66, 16), (17, 19, 1000)]
+
+
+@pytest.mark.parametrize("M,N,K", SHAPES)
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fused_gemm_shapes_transposes_variants(M, N, K, ta, tb):
+    tid = 0x9200 + M + 7 * N + 13 * K
+    A = _mat(K, M, tid) if ta else _mat(M, K, tid)
+    B = _mat(N, K, tid + 1, 0.5) if tb else _mat(K, N, tid + 1, 0.5)
+    ref = oracle.gemm(A, B, bool(ta), bool(tb), fused=True)
+    dA, dB = to_dev(A), to_dev(B)
+    for variant in (0, 1):
+        C = br.repro_gemm_fma(dA, dB, bool(ta), bool(tb), variant=variant)
+        assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant={variant}")
+
+
+def test_fused_witness_and_difference_from_unfused():
+    t = np.float32(1.0 + 2.0 ** -12)
+    A = np.array([[-1.0, t]], np.float32)
+    B = np.array([[1.0], [t]], np.float32)
+    for variant in (0, 1):
+        got = to_host(br.repro_gemm_fma(to_dev(A), to_dev(B), variant=variant))[0, 0]
+        assert got == np.float32(2.0 ** -11 + 2.0 ** -24)
+    # On generic data the fused and unfused chains differ somewhere.
+    A = _mat(64, 256, 0x9300)
+    B = _mat(256, 64, 0x9301)
+    f = to_host(br.repro_gemm_fma(to_dev(A), to_dev(B)))
+    u = to_host(br.repro_gemm(to_dev(A), to_dev(B)))
+    assert (f.view(np.uint32) != u.view(np.uint32)).any()
+
+
+def test_fused_gemm_views_and_subnormals():
+    M, N, K = 70, 90, 50
+    big_a = _mat(M + 3, K + 5, 0x9400)
+    big_b = _mat(K + 2, N + 6, 0x9401)
+    big_a[5:9, 7:20] *= np.float32(2.0 ** -66)
+    big_b[3:30, 2:5] *= np.float32(2.0 ** -66)
+    A = np.ascontiguousarray(big_a[1:1 + M, 3:3 + K])
+    B = np.ascontiguousarray(big_b[2:2 + K, 1:1 + N])
+    ref = oracle.gemm(A, B, fused=True)
+    dA = to_dev(big_a)[1:1 + M, 3:3 + K]
+    dB = to_dev(big_b)[2:2 + K, 1:1 + N]
+    for variant in (0, 1):
+        big_c = torch.zeros((M + 1, N + 9), device="cuda")
+        out = big_c[1:, 3:3 + N]
+        br.repro_gemm_fma(dA, dB, out=out, variant=variant)
+        assert_bitwise(to_host(out), ref, f"views variant {variant}")
+        rest = to_host(big_c).copy()
+        rest[1:, 3:3 + N] = 0
+        assert (rest == 0).all()
+
+
+def test_fused_forward_workload_full_size_sampled():
+    cfg = synth.GEMM
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    print(f"fused gemm workload {M}x{N}x{K}", flush=True)
+    X = synth.gemm_x().reshape(M, K)
+    W = synth.gemm_w().reshape(K, N)
+    dX, dW = to_dev(X), to_dev(W)
+    Y0 = br.repro_gemm_fma(dX, dW, variant=0)
+    Y1 = br.repro_gemm_fma(dX, dW, variant=1)
+    assert torch.equal(Y0.view(torch.int32), Y1.view(torch.int32))
+    C = to_host(Y0)
+    Bt = np.ascontiguousarray(W.T)
+    rng = np.random.default_rng(8)
+    for r in [0, 127, 128, M - 1] + rng.integers(0, M, 2).tolist():
+        assert_bitwise(C[r], oracle.gemm(X[r:r + 1], Bt, trans_b=True, fused=True)[0], f"row {r}")
+    for c in [0, 129, N - 1] + rng.integers(0, N, 1).tolist():
+        assert_bitwise(C[:, c], oracle.gemm(X, Bt[c:c + 1], trans_b=True, fused=True)[:, 0], f"column {c}")
+
+
+def test_fused_dw_workload_sampled():
+    cfg = synth.DW
+    M, N, K = cfg["M"], cfg["N"], cfg["K"]
+    print(f"fused dW workload {M}x{N}x{K}", flush=True)
+    X = synth.dw_x().reshape(K, M)
+    dY = synth.dw_dy().reshape(K, N)
+    dX, ddY = to_dev(X), to_dev(dY)
+    G0 = br.repro_gemm_fma(dX, ddY, trans_a=True, variant=0)
+    G1 = br.repro_gemm_fma(dX, ddY, trans_a=True, variant=1)
+    assert torch.equal(G0.view(torch.int32), G1.view(torch.int32))
+    C = to_host(G0)
+    Aop = np.ascontiguousarray(X.T)
+    Bt = np.ascontiguousarray(dY.T)
+    for r in [0, M - 1, 1000]:
+        assert_bitwise(C[r], oracle.gemm(Aop[r:r + 1], Bt, trans_b=True, fused=True)[0], f"row {r}")
+    for c in [0, N - 1]:
+        assert_bitwise(C[:, c], oracle.gemm(Aop, Bt[c:c + 1], trans_b=True, fused=True)[:, 0], f"column {c}")
+
+
+def test_errors():
+    lib = br.library()
+    d = torch.zeros(64, device="cuda")
+    p = d.data_ptr()
+    assert lib.repro_gemm_fma(0, 0, 2, 2, 2, p, 2, p, 2, p, 2, 2, None) == -1  # no variant 2
+    assert lib.repro_gemm_fma(0, 0, 2, 2, 2, p + 2, 2, p, 2, p, 2, 0, None) == -2
+    assert lib.repro_fp32_fma(p, p, p, p, 4, 2, None) == -1
+    assert lib.repro_fp32_fma(p, p, p + 1, p, 4, 0, None) == -2
+    assert lib.repro_fp32_fma(p, p, p, p, 0, 1, None) == 0

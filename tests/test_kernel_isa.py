@@ -1,0 +1,112 @@
+"""Instruction audit of the library's own kernels (CPU only: hipcc emits the
+gfx950 assembly of our sources, nothing is run).
+
+The binary32 contract keeps multiply and add unfused (OPEN-1B paper, section
+2.1 "Fused multiply-add"): no kernel other than those of the declared fused
+convention may contain a fused or packed fp32 instruction.  The fused-chain
+kernels must contain them, and the matrix-core fused GEMM must do all of its
+arithmetic on the matrix cores.  No kernel may spill to scratch memory.
+"""
+import re
+import sys
+from collections import Counter
+from concurrent.futures import ThreadPoolExecutor
+
+import pytest
+
+sys.path.insert(0, __import__("os").path.join(__import__("os").path.dirname(__file__), "..",
+                                               "bitwise_reproducible_amd", "csrc"))
+import build as lib_build  # noqa: E402
+
+SOURCES = ["gemm.hip", "elementwise.hip", "replay.hip", "state_hash.hip", "fused.hip"]
+FUSED_OR_PACKED = re.compile(r"^v_(fma|fmac|mac|mad)_f32|^v_pk_(fma|add|mul)_f32|^v_(fma|mad)_mix|^v_fma_legacy")
+# Kernels of the declared fused convention.
+FUSED_KERNELS = ("k_gemm_fma", "k_gemm_mfma_fma", "k_fma_valu", "k_fma_mfma")
+
+
+def _kernels(asm: str):
+    out = {}
+    for part in re.split(r"\n(?=_Z[^\s:]+:)", asm):
+        m = re.match(r"(_Z[^\s:]+):", part)
+        if m:
+            body = part.split(".Lfunc_end")[0]
+            out[m.group(1)] = Counter(re.findall(r"^\s+(v_[a-z0-9_]+)", body, re.M))
+    meta = {}
+    for m in re.finditer(r"\.name:\s+(_Z\S+)\n(?:\s+\.[^\n]*\n)*?\s+\.private_segment_fixed_size:\s+(\d+)", asm):
+        meta[m.group(1)] = int(m.group(2))
+    return out, meta
+
+
+def _short(mangled: str) -> str:
+    m = re.search(r"(k_[a-z0-9_]+)", mangled)
+    return m.group(1) if m else mangled
+
+
+@pytest.fixture(scope="module")
+def kernels():
+    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
+        asms = list(ex.map(lib_build.disassemble, SOURCES))
+    ks, meta = {}, {}
+    for a in asms:
+        k, m = _kernels(a)
+        ks.update(k)
+        meta.update(m)
+    assert len(ks) >= 40, sorted(ks)
+    return ks, meta
+
+
+def test_only_fused_convention_kernels_fuse(kernels):
+    # The compiler's correctly rounded division (v_div_scale, v_rcp, fma
+    # refinement, v_div_fmas, v_div_fixup) and square root (v_rsq and fma
+    # refinement) use fused steps internally; those sequences round once to
+    # the IEEE result (checked exhaustively for sqrt and on boundary sets for
+    # division by the GPU tests).  Each may bring at most 5 fused
+    # instructions; every other fused or packed fp32 instruction is an error.
+    ks, _ = kernels
+    for name, ops in ks.items():
+        if _short(name) in FUSED_KERNELS:
+            continue
+        packed = {op: c for op, c in ops.items() if op.startswith("v_pk_")}
+        assert not packed, f"{_short(name)} ({name}) has packed fp32 instructions: {packed}"
+        fused = sum(c for op, c in ops.items() if FUSED_OR_PACKED.match(op))
+        allowed = 5 * (ops["v_div_fixup_f32"] + ops["v_rsq_f32_e32"])
+        assert fused <= allowed, f"{_short(name)} ({name}): {fused} fused instructions, {allowed} allowed"
+        if _short(name).startswith(("k_gemm", "k_tree_reduce", "k_replay", "k_fold", "k_hash")):
+            assert fused == 0, f"{_short(name)} has fused instructions"
+
+
+def test_fused_kernels_use_the_declared_units(kernels):
+    ks, _ = kernels
+    seen = set()
+    for name, ops in ks.items():
+        s = _short(name)
+        if s == "k_gemm_mfma_fma":
+            assert ops["v_mfma_f32_32x32x1_2b_f32"] >= 32
+            assert ops["v_add_f32_e32"] == 0 and ops["v_add_f32_e64"] == 0
+            assert not any(FUSED_OR_PACKED.match(op) for op in ops)
+        elif s == "k_gemm_fma":
+            assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 1024
+            assert ops["v_add_f32_e32"] == 0
+        elif s == "k_fma_mfma":
+            assert ops["v_mfma_f32_32x32x1_2b_f32"] == 1
+        elif s == "k_fma_valu":
+            assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 1
+        else:
+            continue
+        seen.add(s)
+    assert seen == set(FUSED_KERNELS)
+
+
+def test_unfused_gemm_chain_is_one_multiply_and_one_add_per_step(kernels):
+    ks, _ = kernels
+    for name, ops in ks.items():
+        if _short(name) == "k_gemm" and "Li128ELi128ELi16ELi8ELi8E" in name:
+            # 16 k steps x 8 x 8 outputs per lane in the unrolled slab loop.
+            assert ops["v_mul_f32_e32"] >= 1024 and ops["v_add_f32_e32"] >= 1024
+
+
+def test_no_kernel_uses_scratch(kernels):
+    ks, meta = kernels
+    assert set(meta) >= set(ks)
+    spilled = {_short(k): v for k, v in meta.items() if v}
+    assert not spilled, spilled
