@@ -11,7 +11,10 @@
 //    once, so every step is a v_mul_f32 followed by a v_add_f32.  The file
 //    is built with -ffp-contract=off and without packed-fp32 instructions;
 //    the instruction-mix audit in the tests checks that no v_fma / v_fmac /
-//    v_pk_* appears in the kernels.
+//    v_pk_* appears in the unfused kernels.
+//  - repro_gemm_fma declares the other convention (one fused step per k);
+//    its kernels, k_gemm_fma (v_fma_f32) and k_gemm_mfma_fma (matrix cores),
+//    share the tiling below and differ only in the step.
 //  - It is built with -fgpu-flush-denormals-to-zero: the kernel descriptor
 //    sets the fp32 denormal mode to "flush inputs and outputs", so the VALU
 //    itself applies the subnormal rule of section 2.1 at no cost (on gfx950
