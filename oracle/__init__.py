@@ -31,6 +31,9 @@ def _load():
         lib.oracle_gemm.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
         lib.oracle_gemm_fma.argtypes = [ctypes.c_int, ctypes.c_int, i64, i64, i64, vp, i64, vp, i64, vp, i64]
         lib.oracle_fma.argtypes = [vp, vp, vp, vp, i64]
+        lib.oracle_grad_norm.argtypes = [vp, i32, i64, vp]
+        lib.oracle_bf16_round.argtypes = [vp, vp, i64]
+        lib.oracle_adamw_bf16_step.argtypes = [vp, vp, vp, vp, i32, i64, f32, f32, f32, f32, f32, f32, f32, i32, vp]
         lib.oracle_tree_reduce.argtypes = [vp, i32, i64, vp, i32, vp]
         lib.oracle_replay_reduce.argtypes = [vp, i32, i32, i32, i64, vp]
         lib.oracle_fold_push.argtypes = [vp, i32, vp, i64]
@@ -125,6 +128,57 @@ def gemm(A, B, trans_a: bool = False, trans_b: bool = False, fused: bool = False
     _check(fn(int(trans_a), int(trans_b), M, N, K, A.ctypes.data, lda, B.ctypes.data, ldb, C.ctypes.data,
               max(N, 1)), "gemm")
     return C
+
+
+# The optimizer-step record (same field order as the library's).
+STEP_STATE = np.dtype([("step", "<i8"), ("skip_left", "<i4"), ("applied", "<i4"), ("beta1_pow", "<f4"),
+                       ("beta2_pow", "<f4"), ("grad_norm", "<f4"), ("clip_coef", "<f4")])
+
+
+def new_step_state() -> np.ndarray:
+    """A fresh record: no step applied, nothing to skip (all fields zero)."""
+    return np.zeros(1, STEP_STATE)
+
+
+def _grad_arg(g):
+    g = np.ascontiguousarray(g)
+    if g.dtype == np.uint16:  # bf16 bit patterns
+        return g, 1
+    return np.ascontiguousarray(g, np.float32), 0
+
+
+def grad_norm(g, return_sumsq: bool = False):
+    """Pre-clip global l2 norm: sqrt of the TreeFold of the squares (g float32,
+    or uint16 bf16 patterns); with return_sumsq, (norm, S)."""
+    g, dt = _grad_arg(g)
+    out = np.zeros(2, np.float32)
+    _check(_load().oracle_grad_norm(g.ctypes.data, dt, g.size, out.ctypes.data), "grad_norm")
+    return (out[0], out[1]) if return_sumsq else out[0]
+
+
+def bf16_round(x) -> np.ndarray:
+    """binary32 -> bf16 bit patterns (uint16), nearest-even."""
+    x = _f32(x)
+    out = np.empty(x.shape, np.uint16)
+    _check(_load().oracle_bf16_round(x.ctypes.data, out.ctypes.data, x.size), "bf16_round")
+    return out
+
+
+def bf16_widen(h) -> np.ndarray:
+    return (np.ascontiguousarray(h, np.uint16).astype(np.uint32) << 16).view(np.float32)
+
+
+def adamw_bf16_step(w, m, v, g, state, lr, beta1, beta2, eps, weight_decay, max_norm=1.0, spike_threshold=5.0,
+                    skip_steps=5) -> None:
+    """One optimizer step in place: w uint16 (bf16), m and v float32, g float32 or uint16 (bf16)."""
+    assert w.dtype == np.uint16 and m.dtype == np.float32 and v.dtype == np.float32 and state.dtype == STEP_STATE
+    assert w.flags.c_contiguous and m.flags.c_contiguous and v.flags.c_contiguous
+    g, dt = _grad_arg(g)
+    n = w.size
+    assert m.size == n and v.size == n and g.size == n
+    _check(_load().oracle_adamw_bf16_step(w.ctypes.data, m.ctypes.data, v.ctypes.data, g.ctypes.data, dt, n, lr,
+                                          beta1, beta2, eps, weight_decay, max_norm, spike_threshold, skip_steps,
+                                          state.ctypes.data), "adamw_bf16_step")
 
 
 def tree_reduce(replicas, average: bool = True, return_resident: bool = False):

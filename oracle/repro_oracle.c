@@ -434,6 +434,30 @@ static adamw_scalars_t adamw_host_scalars(float beta1, float beta2, int64_t step
     return s;
 }
 
+/* One element of the update: the 16 operations in the order above. */
+static void adamw_element(float w, float m, float v, float g, adamw_scalars_t s, float lr, float beta1,
+                          float beta2, float eps, float weight_decay, float* w_out, float* m_out, float* v_out) {
+    const float m1 = f_mul(beta1, m);
+    const float m2 = f_mul(s.c1, g);
+    const float mn = f_add(m1, m2);
+    const float q = f_mul(g, g);
+    const float v1 = f_mul(beta2, v);
+    const float v2 = f_mul(s.c2, q);
+    const float vn = f_add(v1, v2);
+    const float mh = f_mul(mn, s.r1);
+    const float vh = f_mul(vn, s.r2);
+    const float sq = f_sqrt(vh);
+    const float d = f_add(sq, eps);
+    const float u = f_div(mh, d);
+    const float y = f_mul(weight_decay, w);
+    const float z = f_add(u, y);
+    const float t = f_mul(lr, z);
+    const float wn = f_sub(w, t);
+    *w_out = wn;
+    *m_out = mn;
+    *v_out = vn;
+}
+
 int oracle_adamw_scalars(float beta1, float beta2, int64_t step, float out4[4]) {
     if (step < 1) return ORACLE_EINVAL;
     fpenv_t e = enter_contract();
@@ -454,27 +478,179 @@ int oracle_adamw(float* state, const float* grad, int64_t n, float lr, float bet
     float* V = state + 2 * n;
     for (int64_t i = 0; i < n; ++i) {
         const float g = grad[i], w = W[i], m = Mo[i], v = V[i];
-        const float m1 = f_mul(beta1, m);
-        const float m2 = f_mul(s.c1, g);
-        const float mn = f_add(m1, m2);
-        const float q = f_mul(g, g);
-        const float v1 = f_mul(beta2, v);
-        const float v2 = f_mul(s.c2, q);
-        const float vn = f_add(v1, v2);
-        const float mh = f_mul(mn, s.r1);
-        const float vh = f_mul(vn, s.r2);
-        const float sq = f_sqrt(vh);
-        const float d = f_add(sq, eps);
-        const float u = f_div(mh, d);
-        const float y = f_mul(weight_decay, w);
-        const float z = f_add(u, y);
-        const float t = f_mul(lr, z);
-        const float wn = f_sub(w, t);
+        float wn, mn, vn;
+        adamw_element(w, m, v, g, s, lr, beta1, beta2, eps, weight_decay, &wn, &mn, &vn);
         W[i] = wn;
         Mo[i] = mn;
         V[i] = vn;
     }
     leave_contract(e);
+    return ORACLE_OK;
+}
+/* ------------------------------------------------------------------------ */
+/* BF16 parameters (section 3.1: parameters held in BF16; section 3.2
+ * "Optimizer-state precision": the fused step widens the BF16 parameter and
+ * gradient to FP32, updates in FP32 with FP32 moments, and rounds the
+ * parameter back to BF16 once).  With the global-norm clip (section 3.2,
+ * "Optimizer": gradients clipped to a global l2 norm of 1.0) and the spike
+ * protocol (section 3.4.2: five optimizer steps are skipped when the
+ * pre-clip gradient norm exceeds 5). */
+
+/* bf16 -> binary32: the 16 bits are the high half of the binary32 word. */
+static float bf16_widen(uint16_t h) {
+    uint32_t u = (uint32_t)h << 16;
+    float f;
+    memcpy(&f, &u, 4);
+    return f;
+}
+
+static double f32_bits_to_double(uint32_t u) {
+    float f;
+    memcpy(&f, &u, 4);
+    return (double)f;
+}
+
+/* binary32 -> bf16, round to nearest, ties to even: of the two bf16 values
+ * around x (x truncated toward zero, and the next one away from zero) take
+ * the nearer, by exact binary64 distances; on a tie take the one whose last
+ * kept bit is 0.  x is a normal binary32 value or a zero here (every result
+ * of the update is), so the rounded value is never below 2^-126 unless it is
+ * a zero, and the flush rule has nothing to do. */
+static uint16_t bf16_round(float x) {
+    uint32_t u;
+    memcpy(&u, &x, 4);
+    const uint32_t lo = u & 0xFFFF0000u;
+    const uint32_t hi = lo + 0x10000u;
+    const double ax = fabs((double)x);
+    const double dlo = ax - fabs(f32_bits_to_double(lo));
+    const double dhi = fabs(f32_bits_to_double(hi)) - ax;
+    uint32_t r;
+    if (dlo < dhi) r = lo;
+    else if (dhi < dlo) r = hi;
+    else r = ((lo >> 16) & 1u) == 0 ? lo : hi;
+    return (uint16_t)(r >> 16);
+}
+
+static float load_grad(const void* g, int dtype, int64_t i) {
+    return dtype == 1 ? bf16_widen(((const uint16_t*)g)[i]) : ((const float*)g)[i];
+}
+
+/* Global l2 norm of the gradient, as the pre-clip norm: q_i = g_i * g_i
+ * (binary32, widened first for bf16), S = TreeFold over q_0 .. q_{n-1} in
+ * index order (Appendix A.1's fold, applied to scalars: blocks combined as in
+ * binary counting, lower block on the left, Result from the lowest level
+ * upward), norm = sqrt(S) correctly rounded.  S = 0 for n = 0. */
+static float grad_norm_of(const void* g, int dtype, int64_t n, float* sumsq) {
+    float val[64];
+    int lvl[64];
+    int depth = 0;
+    for (int64_t i = 0; i < n; ++i) {
+        const float x = load_grad(g, dtype, i);
+        float part = f_mul(x, x);
+        int level = 0;
+        while (depth > 0 && lvl[depth - 1] == level) {
+            part = f_add(val[depth - 1], part);
+            --depth;
+            ++level;
+        }
+        val[depth] = part;
+        lvl[depth] = level;
+        ++depth;
+    }
+    float acc = 0.0f;
+    if (depth > 0) {
+        acc = val[depth - 1];
+        for (int d = depth - 2; d >= 0; --d) acc = f_add(acc, val[d]);
+    }
+    if (sumsq) *sumsq = acc;
+    return f_sqrt(acc);
+}
+
+/* out2[0] = the norm, out2[1] = S, the fold of the squares. */
+int oracle_grad_norm(const void* g, int32_t dtype, int64_t n, float* out2) {
+    if (n < 0 || (dtype != 0 && dtype != 1) || (n > 0 && g == NULL)) return ORACLE_EINVAL;
+    fpenv_t e = enter_contract();
+    out2[0] = grad_norm_of(g, dtype, n, &out2[1]);
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* The optimizer-step record kept between steps (mirrors the library's
+ * layout field for field; the oracle has its own definition). */
+typedef struct {
+    int64_t step;      /* updates applied so far */
+    int32_t skip_left; /* steps still to skip */
+    int32_t applied;   /* 1 if the last step applied its update */
+    float beta1_pow;   /* beta1^step (any value while step == 0) */
+    float beta2_pow;
+    float grad_norm;   /* the last step's pre-clip norm */
+    float clip_coef;   /* the coefficient applied to the gradient (1 if none) */
+} oracle_step_state_t;
+
+/* One optimizer step on bf16 parameters w[n], FP32 moments m[n], v[n] and a
+ * gradient g[n] (dtype 0 binary32, 1 bf16), following the recipe:
+ *   norm = the pre-clip global norm above
+ *   spike rule (spike_threshold > 0): norm > spike_threshold starts a
+ *     window of skip_steps skipped steps, this one included (a spike inside
+ *     a window starts it again);
+ *   a skipped step changes neither w, m, v nor the step count;
+ *   clip (max_norm > 0): coef = max_norm / (norm + 1e-6); if coef < 1 every
+ *     gradient element is multiplied by it, one binary32 product each;
+ *   an applied step is step t = step + 1, with beta^t carried as one more
+ *     serial multiply (beta itself at t = 1) and the host scalars of the
+ *     FP32 update, which then runs on (widen(w), m, v, g) and rounds w' to
+ *     bf16 once. */
+int oracle_adamw_bf16_step(uint16_t* w, float* m, float* v, const void* g, int32_t dtype, int64_t n, float lr,
+                           float beta1, float beta2, float eps, float weight_decay, float max_norm,
+                           float spike_threshold, int32_t skip_steps, oracle_step_state_t* st) {
+    if (n < 0 || (dtype != 0 && dtype != 1) || skip_steps < 0 || st == NULL) return ORACLE_EINVAL;
+    if (n > 0 && (w == NULL || m == NULL || v == NULL || g == NULL)) return ORACLE_EINVAL;
+    fpenv_t e = enter_contract();
+    const float norm = grad_norm_of(g, dtype, n, NULL);
+    st->grad_norm = norm;
+    if (spike_threshold > 0.0f && norm > spike_threshold) st->skip_left = skip_steps;
+    int apply = 1;
+    if (st->skip_left > 0) {
+        apply = 0;
+        st->skip_left -= 1;
+    }
+    float coef = 1.0f;
+    if (max_norm > 0.0f) {
+        const float c = f_div(max_norm, f_add(norm, 1e-6f));
+        if (c < 1.0f) coef = c;
+    }
+    st->clip_coef = coef;
+    st->applied = apply;
+    if (apply) {
+        const int64_t t = st->step + 1;
+        const float p1 = t == 1 ? beta1 : f_mul(st->beta1_pow, beta1);
+        const float p2 = t == 1 ? beta2 : f_mul(st->beta2_pow, beta2);
+        adamw_scalars_t s;
+        s.c1 = f_sub(1.0f, beta1);
+        s.c2 = f_sub(1.0f, beta2);
+        s.r1 = f_div(1.0f, f_sub(1.0f, p1));
+        s.r2 = f_div(1.0f, f_sub(1.0f, p2));
+        for (int64_t i = 0; i < n; ++i) {
+            float gi = load_grad(g, dtype, i);
+            if (coef < 1.0f) gi = f_mul(gi, coef);
+            float wn, mn, vn;
+            adamw_element(bf16_widen(w[i]), m[i], v[i], gi, s, lr, beta1, beta2, eps, weight_decay, &wn, &mn, &vn);
+            w[i] = bf16_round(wn);
+            m[i] = mn;
+            v[i] = vn;
+        }
+        st->step = t;
+        st->beta1_pow = p1;
+        st->beta2_pow = p2;
+    }
+    leave_contract(e);
+    return ORACLE_OK;
+}
+
+/* Exported for the pins: bf16 rounding and widening of n values. */
+int oracle_bf16_round(const float* x, uint16_t* out, int64_t n) {
+    if (n < 0) return ORACLE_EINVAL;
+    for (int64_t i = 0; i < n; ++i) out[i] = bf16_round(x[i]);
     return ORACLE_OK;
 }
 

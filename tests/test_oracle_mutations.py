@@ -13,6 +13,7 @@ import oracle
 from oracle import build as oracle_build
 
 import test_oracle_adamw as T_ADAMW
+import test_oracle_adamw_bf16 as T_BF16
 import test_oracle_fma as T_FMA
 import test_oracle_fp32 as T_FP32
 import test_oracle_gemm as T_GEMM
@@ -74,6 +75,20 @@ MUTATIONS = [
      [T_FMA.test_flush_after_rounding_to_24_bits]),
     ("gemm_fma_unfused", "acc = f_fma(a, b, acc);", "acc = f_add(acc, f_mul(a, b));",
      [T_FMA.test_fused_witness]),
+    ("bf16_truncates", "    if (dlo < dhi) r = lo;", "    if (1) r = lo;",
+     [T_BF16.test_bf16_round_matches_torch]),
+    ("norm_result_largest_first",
+     "acc = val[depth - 1];\n        for (int d = depth - 2; d >= 0; --d) acc = f_add(acc, val[d]);",
+     "acc = val[0];\n        for (int d = 1; d < depth; ++d) acc = f_add(acc, val[d]);",
+     [T_BF16.test_fold_result_starts_from_the_smallest_block]),
+    ("skipped_step_applies", "    if (apply) {\n        const int64_t t = st->step + 1;",
+     "    if (1) {\n        const int64_t t = st->step + 1;",
+     [T_BF16.test_spike_protocol_skips_five_steps_without_advancing_the_count]),
+    ("spike_window_not_restarted", "norm > spike_threshold) st->skip_left = skip_steps;",
+     "norm > spike_threshold && st->skip_left == 0) st->skip_left = skip_steps;",
+     [T_BF16.test_spike_inside_the_window_starts_it_again]),
+    ("clip_without_epsilon", "f_div(max_norm, f_add(norm, 1e-6f))", "f_div(max_norm, norm)",
+     [lambda: T_BF16.test_clip_scales_every_element_by_the_coefficient(0.0205)]),
     ("no_flush", "_mm_setcsr((e.saved & ~0x6000u) | 0x8000u | 0x0040u | 0x1F80u);",
      "_mm_setcsr((e.saved & ~(0x6000u | 0x8000u | 0x0040u)) | 0x1F80u);",
      [T_FP32.test_subnormal_results_flush_with_sign, T_FP32.test_subnormal_operands_read_as_signed_zero]),
