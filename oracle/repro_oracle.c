@@ -513,7 +513,7 @@ static double f32_bits_to_double(uint32_t u) {
 /* binary32 -> bf16, round to nearest, ties to even: of the two bf16 values
  * around x (x truncated toward zero, and the next one away from zero) take
  * the nearer, by exact binary64 distances; on a tie take the one whose last
- * kept bit is 0.  x is a normal binary32 value or a zero here (every result
+ * kept bit is 0 (past the largest bf16 this gives infinity, as IEEE does).  x is a normal binary32 value or a zero here (every result
  * of the update is), so the rounded value is never below 2^-126 unless it is
  * a zero, and the flush rule has nothing to do. */
 static uint16_t bf16_round(float x) {
@@ -523,7 +523,11 @@ static uint16_t bf16_round(float x) {
     const uint32_t hi = lo + 0x10000u;
     const double ax = fabs((double)x);
     const double dlo = ax - fabs(f32_bits_to_double(lo));
-    const double dhi = fabs(f32_bits_to_double(hi)) - ax;
+    /* Above the largest bf16 the next value is infinity; the rounding
+     * compares with 2^128, where the unbounded-exponent grid continues
+     * (IEEE 754 overflow: round as if the exponent were unbounded). */
+    const double vhi = ((hi >> 23) & 0xFFu) == 0xFFu ? 0x1p+128 : fabs(f32_bits_to_double(hi));
+    const double dhi = vhi - ax;
     uint32_t r;
     if (dlo < dhi) r = lo;
     else if (dhi < dlo) r = hi;

@@ -36,8 +36,8 @@ def test_bf16_round_matches_torch():
     # next to the smallest normal.
     t = rng.integers(0, 2 ** 31, 10_000).astype(np.uint32) & np.uint32(0xFFFF0000) | np.uint32(0x8000)
     t = t[(((t >> 23) & 0xFF) > 0) & (((t >> 23) & 0xFF) < 0xFF)]  # finite normals
-    edge = np.array([2.0 ** -126, -(2.0 ** -126), 2.0 ** -126 * (1 + 2.0 ** -9), 0.0, -0.0, 1.0, 3.0e38],
-                    np.float32)
+    edge = np.array([2.0 ** -126, -(2.0 ** -126), 2.0 ** -126 * (1 + 2.0 ** -9), 0.0, -0.0, 1.0, 3.0e38,
+                     3.3895e38, -3.3895e38, 3.3961e38, -3.3961e38, 3.4028e38], np.float32)
     for arr in (x, t.view(np.float32), edge):
         np.testing.assert_array_equal(oracle.bf16_round(arr), _torch_bf16(arr))
 
