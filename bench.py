@@ -12,8 +12,10 @@ Each op is bracketed by HIP events on the stream it runs on.  After the
 steps, the audit replay of one step's reduction (OPEN-1B section 6,
 Algorithm 1: 6 replicas x 8 shards x 6 microbatches over an 8,388,608-float
 slice, repro_replay_reduce) and the fused multiply-add GEMM convention
-(repro_gemm_fma on both GEMM workloads, matrix cores and VALU) are timed on
-their own and reported under "next_rows"; they are not part of the step.  `value` is the
+(repro_gemm_fma on both GEMM workloads, matrix cores and VALU) and the
+BF16-parameter optimizer step (repro_adamw_bf16_step: norm, clip, update on
+n = 1.2e9) are timed on their own and reported under "next_rows"; they are
+not part of the step.  `value` is the
 GB/s of the memory-side ops (1, 3, 4: algorithmic bytes over their summed
 event time); the GEMMs are reported in GFLOP/s beside it.  After the timed
 steps the outputs are checked against the CPU oracle (every word of the
@@ -190,6 +192,28 @@ def main():
         up.fill(d, lambda m, offset, out, b=b: synth.replay_grad(b, m, offset=offset, out=out), PC["n"])
         p_grads.append(d)
     p_out = torch.empty(PC["n"], dtype=torch.float32, device=dev)
+    # BF16-parameter optimizer step workload (timed after the steps): the
+    # same n, w bf16, FP32 moments, a bf16 gradient of norm ~3.5 (clipped).
+    bidx = aidx
+    b_w = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    b_g = torch.empty(n, dtype=torch.bfloat16, device=dev)
+    b_m = torch.empty(n, dtype=torch.float32, device=dev)
+    b_v = torch.empty(n, dtype=torch.float32, device=dev)
+    tmp = torch.empty(up.chunk, dtype=torch.float32, device=dev)
+    b_samples = {}
+    for name, dst, gen in (("w", b_w, lambda m_, offset, out: synth.adamw_w(m_, offset=offset, out=out)),
+                           ("g", b_g, lambda m_, offset, out: synth.generate(m_, synth.NORMAL, synth.tid(7, 3), 1e-4,
+                                                                             offset=offset, out=out))):
+        for off in range(0, n, up.chunk):
+            m_ = min(up.chunk, n - off)
+            up.fill(tmp[:m_], lambda mm, offset, out, off=off, gen=gen: gen(mm, offset=off + offset, out=out), m_)
+            dst[off:off + m_].copy_(tmp[:m_])  # round to bf16 (input preparation)
+        b_samples[name] = dst[torch.from_numpy(bidx).to(dev)].view(torch.int16).cpu().numpy().view(np.uint16)
+    b_samples["m"] = up.fill(b_m, lambda m_, offset, out: synth.adamw_m(m_, offset=offset, out=out), n, bidx)
+    b_samples["v"] = up.fill(b_v, lambda m_, offset, out: synth.adamw_v(m_, offset=offset, out=out), n, bidx)
+    del tmp
+    b_state = br.new_step_state(dev)
+    b_ws = br.grad_norm_workspace(n, dev)
     torch.cuda.synchronize()
     del up
     log(f"inputs resident in HBM after {time.time() - t_setup:.1f} s")
@@ -259,6 +283,20 @@ def main():
             fma_ms[(variant, name)] = float(np.mean([f_evs[i].elapsed_time(f_evs[i + 1])
                                                      for i in range(args.steps)]))
 
+    # The BF16 optimizer step, timed on its own.
+    bhp = dict(lr=AC["lr"], beta1=0.9, beta2=0.95, eps=AC["eps"], weight_decay=AC["wd"], max_norm=1.0,
+               spike_threshold=5.0, skip_steps=5)
+    for _ in range(args.warmup):
+        br.repro_adamw_bf16_step(b_w, b_m, b_v, b_g, b_state, workspace=b_ws, **bhp)
+    b_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    b_evs[0].record()
+    for s_ in range(args.steps):
+        br.repro_adamw_bf16_step(b_w, b_m, b_v, b_g, b_state, workspace=b_ws, **bhp)
+        b_evs[s_ + 1].record()
+    torch.cuda.synchronize()
+    bf16_ms = float(np.mean([b_evs[i].elapsed_time(b_evs[i + 1]) for i in range(args.steps)]))
+
     if args.calibration_copy:
         br.repro_tree_reduce([reps[0]], out=g_red, average=False)
         torch.cuda.synchronize()
@@ -304,6 +342,12 @@ def main():
                     f"({p_nbuf} buffers) n={PC['n']}",
         "ms": round(replay_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce")}}
+    bytes_bf16 = 24 * n  # norm pass reads g (2n); update reads w, m, v, g (12n), writes w, m, v (10n)
+    ach = bytes_bf16 / (bf16_ms * 1e-3) / 1e9
+    next_rows["adamw_bf16_step"] = {
+        "workload": f"n={n} bf16 w, fp32 m and v, bf16 g (norm ~3.5, clipped to 1.0), beta2 0.95",
+        "ms": round(bf16_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
     for variant, unit in ((0, "matrix cores, v_mfma_f32_32x32x1_2b_f32"), (1, "VALU, v_fma_f32")):
         ms = fma_ms[(variant, "fwd")] + fma_ms[(variant, "dw")]
         ach = (flops_fwd + flops_dw) / (ms * 1e-3) / 1e12
@@ -330,6 +374,8 @@ def main():
                                  (s_w, s_m, s_v, s_g), hp, AC["step"], args.warmup + args.steps)
         out["verified"].update(verify_replay(np, p_out, p_layout, PC["n"]))
         out["verified"].update(verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f))
+        out["verified"].update(verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, bidx, b_samples, bhp,
+                                           args.warmup + args.steps))
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np)
     print(json.dumps(out), flush=True)
@@ -431,6 +477,35 @@ def verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f):
     bad += int(np.count_nonzero(g[:, 77].view(np.uint32) !=
                                 oracle.gemm(a5, bt5[77:78], trans_b=True, fused=True)[:, 0].view(np.uint32)))
     return {"gemm_fma_sampled_words_differing": bad, "gemm_fma_seconds": round(time.time() - t, 1)}
+
+
+def verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, idx, samples, bhp, nsteps):
+    """The BF16 step: the device norm against the oracle's over the whole
+    gradient, then every step replayed by the oracle on the sampled elements
+    (the gradient is the same each step, so each step applied the same clip
+    coefficient; the oracle applies it first and runs without the rules)."""
+    import oracle
+    t = time.time()
+    g_bits = b_g.view(torch.int16).cpu().numpy().view(np.uint16)
+    norm = oracle.grad_norm(g_bits)
+    del g_bits
+    st = br.read_step_state(b_state)
+    res = {"bf16_norm_matches": bool(np.float32(st["grad_norm"]) == norm),
+           "bf16_steps_applied": int(st["step"])}
+    coef = np.float32(1.0) / (norm + np.float32(1e-6))
+    gc = (oracle.bf16_widen(samples["g"]) * coef).astype(np.float32) if coef < 1 else oracle.bf16_widen(samples["g"])
+    w, m, v = samples["w"].copy(), samples["m"].copy(), samples["v"].copy()
+    so = oracle.new_step_state()
+    hp = {k: bhp[k] for k in ("lr", "beta1", "beta2", "eps", "weight_decay")}
+    for _ in range(nsteps):
+        oracle.adamw_bf16_step(w, m, v, gc, so, **hp, max_norm=0.0, spike_threshold=0.0)
+    tidx = torch.from_numpy(idx).to(b_w.device)
+    bad = int(np.count_nonzero(b_w[tidx].view(torch.int16).cpu().numpy().view(np.uint16) != w))
+    bad += int(np.count_nonzero(b_m[tidx].cpu().numpy().view(np.uint32) != m.view(np.uint32)))
+    bad += int(np.count_nonzero(b_v[tidx].cpu().numpy().view(np.uint32) != v.view(np.uint32)))
+    res["bf16_sampled_words_differing"] = bad
+    res["bf16_seconds"] = round(time.time() - t, 1)
+    return res
 
 
 def cpu_baseline(np):

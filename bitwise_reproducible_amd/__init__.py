@@ -15,6 +15,9 @@ Entry points (same names as the C ABI):
     repro_state_hash(words, workspace=None) -> 32-byte digest (bytes)
     repro_state_hash_async(words, digest_out, workspace)
     repro_fp32_ops(op, a, b, out=None);  repro_fp32_fma(a, b, c, unit=0, out=None)
+    repro_grad_norm(grad, workspace=None, out=None) -> device tensor [norm, S]
+    repro_adamw_bf16_step(w, m, v, grad, state, lr, beta1, beta2, eps, weight_decay,
+                          max_norm=1.0, spike_threshold=5.0, skip_steps=5, workspace=None)
 """
 from __future__ import annotations
 
@@ -65,11 +68,17 @@ def library():
         lib.repro_fold_push.argtypes = [vp, i32, vp, i64, vp]
         lib.repro_fold_result.argtypes = [vp, i32, i64, vp, i32, vp]
         lib.repro_gemm_fma.argtypes = gemm_args + [i32, vp]
+        lib.repro_grad_norm_workspace_bytes.restype = i64
+        lib.repro_grad_norm_workspace_bytes.argtypes = [i64]
+        lib.repro_grad_norm.argtypes = [vp, i32, i64, vp, i64, vp, vp]
+        f32 = ctypes.c_float
+        lib.repro_adamw_bf16_step.argtypes = [vp, vp, vp, vp, i32, i64, f32, f32, f32, f32, f32, f32, f32, i32, vp,
+                                              i64, vp, vp]
         lib.repro_fp32_fma.argtypes = [vp, vp, vp, vp, i64, i32, vp]
         for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
                      "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops",
                      "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_gemm_fma",
-                     "repro_fp32_fma"):
+                     "repro_fp32_fma", "repro_grad_norm", "repro_adamw_bf16_step"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -304,6 +313,77 @@ def repro_fp32_fma(a, b, c, unit: int = 0, out=None, stream=None):
     return out
 
 
-__all__ = ["repro_gemm", "repro_gemm_fma", "repro_fp32_fma", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
+REPRO_GRAD_F32, REPRO_GRAD_BF16 = 0, 1
+STEP_STATE_BYTES = 32
+# Field layout of repro_step_state (include/repro.h).
+STEP_STATE_FIELDS = [("step", "<i8"), ("skip_left", "<i4"), ("applied", "<i4"), ("beta1_pow", "<f4"),
+                     ("beta2_pow", "<f4"), ("grad_norm", "<f4"), ("clip_coef", "<f4")]
+
+
+def _grad_dtype(g):
+    import torch
+    if g.dtype == torch.bfloat16:
+        return REPRO_GRAD_BF16
+    if g.dtype == torch.float32:
+        return REPRO_GRAD_F32
+    raise TypeError("grad must be float32 or bfloat16")
+
+
+def grad_norm_workspace(n: int, device="cuda"):
+    import torch
+    nbytes = int(library().repro_grad_norm_workspace_bytes(int(n)))
+    if nbytes < 0:
+        raise ValueError("bad size")
+    return torch.empty(nbytes, dtype=torch.uint8, device=device)
+
+
+def new_step_state(device="cuda"):
+    """A zeroed repro_step_state in device memory (no step taken yet)."""
+    import torch
+    return torch.zeros(STEP_STATE_BYTES, dtype=torch.uint8, device=device)
+
+
+def read_step_state(state) -> dict:
+    """Host copy of a device repro_step_state as a dict."""
+    import numpy as np
+    rec = state.cpu().numpy().view(np.dtype(STEP_STATE_FIELDS))[0]
+    return {name: rec[name].item() for name, _ in STEP_STATE_FIELDS}
+
+
+def repro_grad_norm(grad, workspace=None, out=None, stream=None):
+    """Device tensor [norm, S]: the pre-clip global norm of a flat float32 or bfloat16 gradient."""
+    import torch
+    if not grad.is_contiguous():
+        raise ValueError("grad must be contiguous")
+    if workspace is None:
+        workspace = grad_norm_workspace(grad.numel(), grad.device)
+    if out is None:
+        out = torch.empty(2, dtype=torch.float32, device=grad.device)
+    _check(library().repro_grad_norm(grad.data_ptr(), _grad_dtype(grad), grad.numel(), workspace.data_ptr(),
+                                     workspace.numel(), out.data_ptr(), _stream(stream)), "repro_grad_norm")
+    return out
+
+
+def repro_adamw_bf16_step(w, m, v, grad, state, lr: float, beta1: float, beta2: float, eps: float,
+                          weight_decay: float, max_norm: float = 1.0, spike_threshold: float = 5.0,
+                          skip_steps: int = 5, workspace=None, stream=None):
+    """One BF16-parameter optimizer step in place (w bfloat16; m, v float32; grad float32 or bfloat16)."""
+    import torch
+    if w.dtype != torch.bfloat16 or m.dtype != torch.float32 or v.dtype != torch.float32:
+        raise TypeError("w must be bfloat16, m and v float32")
+    n = w.numel()
+    for t, nm in ((w, "w"), (m, "m"), (v, "v"), (grad, "grad")):
+        if not t.is_contiguous() or t.numel() != n or not t.is_cuda:
+            raise ValueError(f"{nm} must be a contiguous device tensor of {n} elements")
+    if workspace is None:
+        workspace = grad_norm_workspace(n, w.device)
+    _check(library().repro_adamw_bf16_step(w.data_ptr(), m.data_ptr(), v.data_ptr(), grad.data_ptr(),
+                                           _grad_dtype(grad), n, lr, beta1, beta2, eps, weight_decay, max_norm,
+                                           spike_threshold, int(skip_steps), workspace.data_ptr(), workspace.numel(),
+                                           state.data_ptr(), _stream(stream)), "repro_adamw_bf16_step")
+
+
+__all__ = ["repro_gemm", "repro_grad_norm", "repro_adamw_bf16_step", "new_step_state", "read_step_state",
+           "grad_norm_workspace", "repro_gemm_fma", "repro_fp32_fma", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
            "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
            "ReproError", "LIB_PATH"]

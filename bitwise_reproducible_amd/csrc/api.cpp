@@ -238,6 +238,63 @@ int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64
   return status_of(repro::launch_fp32_ops(op, a, b, out, n, static_cast<hipStream_t>(stream)));
 }
 
+int64_t repro_grad_norm_workspace_bytes(int64_t n) {
+  if (n < 0) return REPRO_EINVAL;
+  repro::NormPlan plan;
+  repro::plan_grad_norm(n, &plan);
+  return plan.total_bytes;
+}
+
+namespace {
+
+int check_grad(const void* grad, int32_t dtype, int64_t n, void* workspace, int64_t ws_bytes,
+               repro::NormPlan* plan) {
+  if (n < 0 || (dtype != REPRO_GRAD_F32 && dtype != REPRO_GRAD_BF16) || workspace == nullptr) return REPRO_EINVAL;
+  if (n > 0 && grad == nullptr) return REPRO_EINVAL;
+  if (n > 0 && (reinterpret_cast<uintptr_t>(grad) & (dtype == REPRO_GRAD_BF16 ? 1u : 3u)) != 0) return REPRO_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 255u) != 0) return REPRO_EALIGN;
+  repro::plan_grad_norm(n, plan);
+  if (ws_bytes < plan->total_bytes) return REPRO_ESPACE;
+  return REPRO_OK;
+}
+
+}  // namespace
+
+int repro_grad_norm(const void* grad, int32_t grad_dtype, int64_t n, void* workspace, int64_t ws_bytes,
+                    float* out2, void* stream) {
+  repro::NormPlan plan;
+  const int st = check_grad(grad, grad_dtype, n, workspace, ws_bytes, &plan);
+  if (st != REPRO_OK) return st;
+  if (out2 == nullptr) return REPRO_EINVAL;
+  if (!aligned4(out2)) return REPRO_EALIGN;
+  const repro::StepRule rule = {0.0f, 0.0f, 0.0f, 0.0f, 0};
+  return status_of(repro::launch_grad_norm(grad, grad_dtype, n, static_cast<uint8_t*>(workspace), plan, out2,
+                                           nullptr, rule, static_cast<hipStream_t>(stream)));
+}
+
+int repro_adamw_bf16_step(uint16_t* w, float* m, float* v, const void* grad, int32_t grad_dtype, int64_t n,
+                          float lr, float beta1, float beta2, float eps, float weight_decay, float max_norm,
+                          float spike_threshold, int32_t skip_steps, void* workspace, int64_t ws_bytes,
+                          repro_step_state* state, void* stream) {
+  repro::NormPlan plan;
+  const int st = check_grad(grad, grad_dtype, n, workspace, ws_bytes, &plan);
+  if (st != REPRO_OK) return st;
+  if (state == nullptr || skip_steps < 0) return REPRO_EINVAL;
+  if ((reinterpret_cast<uintptr_t>(state) & 7u) != 0) return REPRO_EALIGN;
+  if (n > 0) {
+    if (w == nullptr || m == nullptr || v == nullptr) return REPRO_EINVAL;
+    if ((reinterpret_cast<uintptr_t>(w) & 1u) != 0 || !aligned4(m) || !aligned4(v)) return REPRO_EALIGN;
+  }
+  const hipStream_t s = static_cast<hipStream_t>(stream);
+  const repro::StepRule rule = {beta1, beta2, max_norm, spike_threshold, skip_steps};
+  hipError_t e = repro::launch_grad_norm(grad, grad_dtype, n, static_cast<uint8_t*>(workspace), plan, nullptr, state,
+                                         rule, s);
+  if (e != hipSuccess) return status_of(e);
+  if (n == 0) return REPRO_OK;
+  return status_of(repro::launch_adamw_bf16(w, m, v, grad, grad_dtype, n, static_cast<const uint8_t*>(workspace), lr,
+                                            beta1, beta2, eps, weight_decay, s));
+}
+
 int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
                    void* stream) {
   if (unit < 0 || unit > 1 || n < 0) return REPRO_EINVAL;

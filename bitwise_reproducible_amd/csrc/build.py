@@ -37,6 +37,7 @@ SOURCES = {
     "state_hash.hip": [],
     "replay.hip": [],
     "fused.hip": [],
+    "optimizer.hip": [],
 }
 
 

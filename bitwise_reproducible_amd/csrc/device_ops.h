@@ -7,6 +7,8 @@
 
 #include <hip/hip_runtime.h>
 
+#include "internal.h"
+
 namespace repro {
 namespace {
 
@@ -38,6 +40,32 @@ __device__ __forceinline__ float add_v(float a, float b) { return add_c(a, b); }
 __device__ __forceinline__ float4 add_v(float4 a, float4 b) { return add4(a, b); }
 __device__ __forceinline__ float mul_vs(float a, float s) { return mul_c(a, s); }
 __device__ __forceinline__ float4 mul_vs(float4 a, float s) { return mul4s(a, s); }
+
+// AdamW ("OPEN-1B: A Fully Auditable Training Run", section 3.2
+// "Optimizer"): the sixteen operations in their declared order, each one
+// rounding, with the host scalars c1 = 1 - beta1, c2 = 1 - beta2 and the
+// bias-correction reciprocals r1, r2.
+__device__ __forceinline__ void adamw_elem(float& w, float& m, float& v, float g, const AdamwScalars& s) {
+  const float m1 = mul_c(s.beta1, m);
+  const float m2 = mul_c(s.c1, g);
+  const float mn = add_c(m1, m2);
+  const float q = mul_c(g, g);
+  const float v1 = mul_c(s.beta2, v);
+  const float v2 = mul_c(s.c2, q);
+  const float vn = add_c(v1, v2);
+  const float mh = mul_c(mn, s.r1);
+  const float vh = mul_c(vn, s.r2);
+  const float sq = sqrt_c(vh);
+  const float d = add_c(sq, s.eps);
+  const float u = div_c(mh, d);
+  const float y = mul_c(s.wd, w);
+  const float z = add_c(u, y);
+  const float t = mul_c(s.lr, z);
+  const float wn = sub_c(w, t);
+  w = wn;
+  m = mn;
+  v = vn;
+}
 
 }  // namespace
 }  // namespace repro

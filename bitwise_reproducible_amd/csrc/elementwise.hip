@@ -152,30 +152,7 @@ int64_t grid_for(int64_t items, int threads, int64_t cap) {
 bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) == 0; }
 
 // ---------------------------------------------------------------------------
-// AdamW (section 3.2 "Optimizer"): the sixteen operations in their declared
-// order, each one rounding.
-__device__ __forceinline__ void adamw_elem(float& w, float& m, float& v, float g, const AdamwScalars& s) {
-  const float m1 = mul_c(s.beta1, m);
-  const float m2 = mul_c(s.c1, g);
-  const float mn = add_c(m1, m2);
-  const float q = mul_c(g, g);
-  const float v1 = mul_c(s.beta2, v);
-  const float v2 = mul_c(s.c2, q);
-  const float vn = add_c(v1, v2);
-  const float mh = mul_c(mn, s.r1);
-  const float vh = mul_c(vn, s.r2);
-  const float sq = sqrt_c(vh);
-  const float d = add_c(sq, s.eps);
-  const float u = div_c(mh, d);
-  const float y = mul_c(s.wd, w);
-  const float z = add_c(u, y);
-  const float t = mul_c(s.lr, z);
-  const float wn = sub_c(w, t);
-  w = wn;
-  m = mn;
-  v = vn;
-}
-
+// AdamW (section 3.2 "Optimizer"): adamw_elem in device_ops.h.
 __global__ __launch_bounds__(256) void k_adamw_v4(float4* __restrict__ w4, float4* __restrict__ m4,
                                                    float4* __restrict__ v4, const float4* __restrict__ g4,
                                                    int64_t n4, AdamwScalars s) {

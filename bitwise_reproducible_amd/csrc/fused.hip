@@ -27,16 +27,16 @@ namespace {
 
 typedef float floatx32 __attribute__((ext_vector_type(32)));
 
-__global__ __launch_bounds__(256) void k_fma_valu(const float* __restrict__ a, const float* __restrict__ b,
-                                                  const float* __restrict__ c, float* __restrict__ out,
+__global__ __launch_bounds__(256) void k_fma_valu(const float* a, const float* b,
+                                                  const float* c, float* out,
                                                   int64_t n) {
   const int64_t stride = (int64_t)gridDim.x * blockDim.x;
   for (int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x; i < n; i += stride)
     out[i] = __builtin_fmaf(a[i], b[i], c[i]);
 }
 
-__global__ __launch_bounds__(256) void k_fma_mfma(const float* __restrict__ a, const float* __restrict__ b,
-                                                  const float* __restrict__ c, float* __restrict__ out,
+__global__ __launch_bounds__(256) void k_fma_mfma(const float* a, const float* b,
+                                                  const float* c, float* out,
                                                   int64_t n) {
   const int lane = threadIdx.x & 63;
   const int64_t groups = (n + 63) / 64;

@@ -50,6 +50,32 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
                        const float* B, int64_t ldb, float* C, int64_t ldc, int variant, bool fused,
                        hipStream_t stream);
 
+// optimizer.hip
+struct OptHeader {  // first bytes of the grad-norm / optimizer workspace
+  float norm;       // the pre-clip global norm
+  float sumsq;      // the fold of the squares
+  int apply;        // 1: the step applies its update
+  float coef;       // clip coefficient (1: no clip)
+  float c1, c2, r1, r2;
+};
+constexpr int64_t kOptHeaderBytes = 256;
+struct NormPlan {
+  static constexpr int kMaxPasses = 8;
+  int passes;
+  int64_t len[kMaxPasses];         // input length of each pass
+  int64_t out_offset[kMaxPasses];  // workspace offset of its block sums (-1: the header)
+  int64_t total_bytes;
+};
+struct StepRule {
+  float beta1, beta2, max_norm, spike_threshold;
+  int skip_steps;
+};
+void plan_grad_norm(int64_t n, NormPlan* plan);
+hipError_t launch_grad_norm(const void* g, int dtype, int64_t n, uint8_t* ws, const NormPlan& plan, float* out2,
+                            repro_step_state* st, const StepRule& rule, hipStream_t stream);
+hipError_t launch_adamw_bf16(uint16_t* w, float* m, float* v, const void* g, int dtype, int64_t n, const uint8_t* ws,
+                             float lr, float beta1, float beta2, float eps, float wd, hipStream_t stream);
+
 // fused.hip
 hipError_t launch_fp32_fma(int unit, const float* a, const float* b, const float* c, float* out, int64_t n,
                            hipStream_t stream);

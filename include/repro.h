@@ -53,7 +53,7 @@ extern "C" {
 #define REPRO_EINVAL -1 /* null pointer, negative size, bad flag, R out of range, ld too small, step < 1 */
 #define REPRO_EALIGN -2 /* a device pointer is not 4-byte aligned */
 #define REPRO_EDEVICE -3 /* HIP launch or runtime error */
-#define REPRO_ESPACE -4 /* hash workspace too small */
+#define REPRO_ESPACE -4 /* workspace too small */
 
 #define REPRO_MAX_REPLICAS 64
 #define REPRO_MAX_REPLAY_BUFFERS 384
@@ -220,6 +220,83 @@ int repro_adamw_variant(float* state, const float* grad, int64_t n, float lr, fl
                         float eps, float weight_decay, int64_t step, int32_t variant, void* stream);
 
 /*
+ * BF16-parameter optimizer step with the global-norm clip and the spike rule.
+ *
+ * Paper section 3.1 (parameters held in BF16, FP32 gradient reduction),
+ * section 3.2 "Optimizer" (AdamW; gradients clipped to a global l2 norm of
+ * 1.0) and "Optimizer-state precision" (the fused step widens the BF16
+ * parameter and gradient to FP32, updates in FP32 with FP32 moments, rounds
+ * the parameter to BF16 once), section 3.4.2 (five optimizer steps are
+ * skipped when the pre-clip gradient norm exceeds 5).
+ *
+ * The pre-clip norm: q_i = g_i * g_i in binary32 (bf16 gradients widened
+ * first), S = TreeFold(q_0, ..., q_{n-1}) in index order (Appendix A.1's
+ * fold applied to scalars: equal blocks combined as in binary counting,
+ * Result from the smallest block upward), norm = sqrt(S) correctly rounded.
+ *
+ * One step, all in binary32 under the contract:
+ *   spike rule (spike_threshold > 0): norm > spike_threshold sets
+ *     skip_left = skip_steps, so this step and the next skip_steps - 1 are
+ *     skipped (a spike inside the window starts it again);
+ *   skipped (skip_left > 0, then decremented): w, m, v and step unchanged;
+ *   clip (max_norm > 0): c = max_norm / (norm + 1e-6); when c < 1 every
+ *     gradient element is multiplied by c (one product each);
+ *   applied: t = step + 1, beta^t carried as one more serial multiply of
+ *     beta_pow (beta itself at t = 1), c1, c2, r1 = 1/(1 - beta1^t),
+ *     r2 = 1/(1 - beta2^t), then per element the sixteen operations of
+ *     repro_adamw on (widen(w), m, v, g), and w' rounded to bf16 (nearest,
+ *     ties to even) once.
+ */
+typedef struct repro_step_state {
+  int64_t step;      /* updates applied so far */
+  int32_t skip_left; /* steps still to skip */
+  int32_t applied;   /* 1 if the last step applied its update */
+  float beta1_pow;   /* beta1^step (not read while step == 0) */
+  float beta2_pow;   /* beta2^step */
+  float grad_norm;   /* the last step's pre-clip norm */
+  float clip_coef;   /* the coefficient applied to its gradient (1: none) */
+} repro_step_state;  /* 32 bytes; all zero = no step taken yet */
+
+#define REPRO_GRAD_F32 0
+#define REPRO_GRAD_BF16 1
+
+/* Workspace bytes for n gradient elements (block sums of the norm's fold
+ * and the step's scalars); at least 256. */
+int64_t repro_grad_norm_workspace_bytes(int64_t n);
+
+/*
+ * repro_grad_norm: out2[0] = the pre-clip norm above, out2[1] = S.
+ *   grad:      device pointer to n elements of grad_dtype (REPRO_GRAD_F32,
+ *              4-byte aligned, or REPRO_GRAD_BF16, 2-byte aligned).
+ *   workspace: device memory, 256-byte aligned, of at least
+ *              repro_grad_norm_workspace_bytes(n) bytes (REPRO_ESPACE
+ *              otherwise).
+ *   out2:      device pointer to 2 floats, written last.
+ * n == 0: norm = S = 0.  Asynchronous on the stream.
+ */
+int repro_grad_norm(const void* grad, int32_t grad_dtype, int64_t n, void* workspace, int64_t ws_bytes,
+                    float* out2, void* stream);
+
+/*
+ * repro_adamw_bf16_step: one optimizer step, in place and asynchronous.
+ *   w:     device pointer to n bf16 parameters (uint16 bit patterns).
+ *   m, v:  device pointers to n floats each (FP32 moments).
+ *   grad:  as repro_grad_norm; must not overlap w, m or v.
+ *   max_norm <= 0 disables the clip, spike_threshold <= 0 the spike rule;
+ *   skip_steps >= 0.
+ *   workspace: as repro_grad_norm.
+ *   state: device pointer to the caller's repro_step_state (8-byte
+ *          aligned), read and updated by the step; zero it before the first.
+ * The step count, the skip window and the beta powers live in `state`, so
+ * consecutive calls need no host synchronisation.  Calls that share a
+ * workspace or a state must be ordered on one stream.
+ */
+int repro_adamw_bf16_step(uint16_t* w, float* m, float* v, const void* grad, int32_t grad_dtype, int64_t n,
+                          float lr, float beta1, float beta2, float eps, float weight_decay, float max_norm,
+                          float spike_threshold, int32_t skip_steps, void* workspace, int64_t ws_bytes,
+                          repro_step_state* state, void* stream);
+
+/*
  * repro_state_hash: 32-byte BLAKE2b tree digest of n_words binary32 words.
  *
  * Paper Appendix B (a canonical per-step state hash) and Figure 11 (the hash
@@ -262,8 +339,7 @@ int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64
  * core instruction v_mfma_f32_32x32x1_2b_f32 (each element placed on the
  * diagonal of a 32x32 block, with c[i] as the C operand).  For directed
  * tests of the single step each fused GEMM variant repeats.  Device pointers
- * of n floats; out may equal a, b or c only if it equals all the inputs it
- * overlaps element for element.
+ * of n floats; out may be the same pointer as a, b or c (no partial overlap).
  */
 int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
                    void* stream);
