@@ -12,8 +12,9 @@ Each op is bracketed by HIP events on the stream it runs on.  After the
 steps, the audit replay of one step's reduction (OPEN-1B section 6,
 Algorithm 1: 6 replicas x 8 shards x 6 microbatches over an 8,388,608-float
 slice, repro_replay_reduce) and the fused multiply-add GEMM convention
-(repro_gemm_fma on both GEMM workloads, matrix cores and VALU) and the
-BF16-parameter optimizer step (repro_adamw_bf16_step: norm, clip, update on
+(repro_gemm_fma on both GEMM workloads, matrix cores and VALU), AdamW with
+the state hash overlapped (repro_adamw_hash) and the BF16-parameter
+optimizer step (repro_adamw_bf16_step: norm, clip, update on
 n = 1.2e9) are timed on their own and reported under "next_rows"; they are
 not part of the step.  `value` is the
 GB/s of the memory-side ops (1, 3, 4: algorithmic bytes over their summed
@@ -283,6 +284,25 @@ def main():
             fma_ms[(variant, name)] = float(np.mean([f_evs[i].elapsed_time(f_evs[i + 1])
                                                      for i in range(args.steps)]))
 
+    # AdamW and the state hash overlapped (repro_adamw_hash), on a copy of
+    # the optimizer state that continues from the steps' last step counter.
+    state2 = state.clone()
+    ws2 = br.hash_workspace(3 * n, dev)  # the steps' leaf digests in ws are checked later
+    digest2 = torch.empty(32, dtype=torch.uint8, device=dev)
+    ah_step0 = step_counter[0]
+    for _ in range(args.warmup):
+        br.repro_adamw_hash(state2, grad, digest2, ws2, step=step_counter[0], **hp)
+        step_counter[0] += 1
+    ah_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    torch.cuda.synchronize()
+    ah_evs[0].record()
+    for s_ in range(args.steps):
+        br.repro_adamw_hash(state2, grad, digest2, ws2, step=step_counter[0], **hp)
+        step_counter[0] += 1
+        ah_evs[s_ + 1].record()
+    torch.cuda.synchronize()
+    ah_ms = float(np.mean([ah_evs[i].elapsed_time(ah_evs[i + 1]) for i in range(args.steps)]))
+
     # The BF16 optimizer step, timed on its own.
     bhp = dict(lr=AC["lr"], beta1=0.9, beta2=0.95, eps=AC["eps"], weight_decay=AC["wd"], max_norm=1.0,
                spike_threshold=5.0, skip_steps=5)
@@ -342,6 +362,12 @@ def main():
                     f"({p_nbuf} buffers) n={PC['n']}",
         "ms": round(replay_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce")}}
+    ach = (bytes_adamw + bytes_hash) / (ah_ms * 1e-3) / 1e9
+    next_rows["adamw_hash_overlapped"] = {
+        "workload": "the adamw + state_hash workload in one call, update chunks of 2^26 elements overlapped with "
+                    "the hash of the chunk before on a second stream",
+        "ms": round(ah_ms, 4), "ms_in_turn": round(op_ms["adamw"] + op_ms["state_hash"], 4),
+        "achieved": round(ach, 1), "unit": "GB/s", "bytes": bytes_adamw + bytes_hash}
     bytes_bf16 = 24 * n  # norm pass reads g (2n); update reads w, m, v, g (12n), writes w, m, v (10n)
     ach = bytes_bf16 / (bf16_ms * 1e-3) / 1e9
     next_rows["adamw_bf16_step"] = {
@@ -374,6 +400,8 @@ def main():
                                  (s_w, s_m, s_v, s_g), hp, AC["step"], args.warmup + args.steps)
         out["verified"].update(verify_replay(np, p_out, p_layout, PC["n"]))
         out["verified"].update(verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f))
+        out["verified"].update(verify_adamw_hash(np, torch, br, state2, digest2, ws2, n, aidx, (s_w, s_m, s_v, s_g),
+                                                 hp, AC["step"], ah_step0, step_counter[0]))
         out["verified"].update(verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, bidx, b_samples, bhp,
                                            args.warmup + args.steps))
     if not args.no_cpu_baseline:
@@ -477,6 +505,26 @@ def verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f):
     bad += int(np.count_nonzero(g[:, 77].view(np.uint32) !=
                                 oracle.gemm(a5, bt5[77:78], trans_b=True, fused=True)[:, 0].view(np.uint32)))
     return {"gemm_fma_sampled_words_differing": bad, "gemm_fma_seconds": round(time.time() - t, 1)}
+
+
+def verify_adamw_hash(np, torch, br, state2, digest2, ws, n, aidx, samples, hp, step0, ah_step0, ah_end):
+    """The overlapped calls: every AdamW step of the run replayed by the
+    oracle on the sampled elements (the steps', then the overlapped calls'),
+    and the last digest against a separate hash of the final state."""
+    import oracle
+    t = time.time()
+    s_w, s_m, s_v, s_g = samples
+    st = np.concatenate([s_w, s_m, s_v]).astype(np.float32)
+    for t_ in range(step0, ah_end):  # the steps' updates (to ah_step0), then the overlapped calls'
+        oracle.adamw_inplace(st, s_g, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], t_)
+    tidx = torch.from_numpy(aidx).to(state2.device)
+    got = np.concatenate([state2[:n][tidx].cpu().numpy(), state2[n:2 * n][tidx].cpu().numpy(),
+                          state2[2 * n:][tidx].cpu().numpy()])
+    d = torch.empty(32, dtype=torch.uint8, device=state2.device)
+    br.repro_state_hash_async(state2, d, ws)
+    return {"adamw_hash_sampled_words_differing": int(np.count_nonzero(got.view(np.uint32) != st.view(np.uint32))),
+            "adamw_hash_digest_matches": bool(torch.equal(d, digest2)),
+            "adamw_hash_seconds": round(time.time() - t, 1)}
 
 
 def verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, idx, samples, bhp, nsteps):

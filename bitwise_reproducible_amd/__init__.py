@@ -15,6 +15,7 @@ Entry points (same names as the C ABI):
     repro_state_hash(words, workspace=None) -> 32-byte digest (bytes)
     repro_state_hash_async(words, digest_out, workspace)
     repro_fp32_ops(op, a, b, out=None);  repro_fp32_fma(a, b, c, unit=0, out=None)
+    repro_adamw_hash(state, grad, digest_out, workspace, lr, beta1, beta2, eps, weight_decay, step, chunk=0)
     repro_grad_norm(grad, workspace=None, out=None) -> device tensor [norm, S]
     repro_adamw_bf16_step(w, m, v, grad, state, lr, beta1, beta2, eps, weight_decay,
                           max_norm=1.0, spike_threshold=5.0, skip_steps=5, workspace=None)
@@ -68,6 +69,8 @@ def library():
         lib.repro_fold_push.argtypes = [vp, i32, vp, i64, vp]
         lib.repro_fold_result.argtypes = [vp, i32, i64, vp, i32, vp]
         lib.repro_gemm_fma.argtypes = gemm_args + [i32, vp]
+        lib.repro_adamw_hash.argtypes = [vp, vp, i64, ctypes.c_float, ctypes.c_float, ctypes.c_float,
+                                         ctypes.c_float, ctypes.c_float, i64, vp, i64, vp, i64, vp]
         lib.repro_grad_norm_workspace_bytes.restype = i64
         lib.repro_grad_norm_workspace_bytes.argtypes = [i64]
         lib.repro_grad_norm.argtypes = [vp, i32, i64, vp, i64, vp, vp]
@@ -78,7 +81,7 @@ def library():
         for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
                      "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops",
                      "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_gemm_fma",
-                     "repro_fp32_fma", "repro_grad_norm", "repro_adamw_bf16_step"):
+                     "repro_fp32_fma", "repro_grad_norm", "repro_adamw_bf16_step", "repro_adamw_hash"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -283,6 +286,17 @@ def repro_state_hash(words, workspace=None, stream=None) -> bytes:
     return bytes(digest.cpu().numpy().tobytes())
 
 
+def repro_adamw_hash(state, grad, digest_out, workspace, lr: float, beta1: float, beta2: float, eps: float,
+                     weight_decay: float, step: int, chunk: int = 0, stream=None):
+    """repro_adamw then the state hash of the updated state, overlapped (see repro.h)."""
+    n = grad.numel()
+    if state.numel() != 3 * n or not state.is_contiguous() or not grad.is_contiguous():
+        raise ValueError("state must hold 3n contiguous floats for a grad of n")
+    _check(library().repro_adamw_hash(state.data_ptr(), grad.data_ptr(), n, lr, beta1, beta2, eps, weight_decay,
+                                      int(step), workspace.data_ptr(), workspace.numel(), digest_out.data_ptr(),
+                                      int(chunk), _stream(stream)), "repro_adamw_hash")
+
+
 def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
     """One contract operation per element (diagnostic; see repro.h)."""
     import torch
@@ -383,7 +397,7 @@ def repro_adamw_bf16_step(w, m, v, grad, state, lr: float, beta1: float, beta2: 
                                            state.data_ptr(), _stream(stream)), "repro_adamw_bf16_step")
 
 
-__all__ = ["repro_gemm", "repro_grad_norm", "repro_adamw_bf16_step", "new_step_state", "read_step_state",
+__all__ = ["repro_gemm", "repro_adamw_hash", "repro_grad_norm", "repro_adamw_bf16_step", "new_step_state", "read_step_state",
            "grad_norm_workspace", "repro_gemm_fma", "repro_fp32_fma", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
            "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
            "ReproError", "LIB_PATH"]

@@ -6,6 +6,9 @@
 #include <stdint.h>
 #include <xmmintrin.h>
 
+#include <mutex>
+#include <vector>
+
 #include "internal.h"
 #include "repro.h"
 
@@ -207,6 +210,108 @@ int repro_adamw_variant(float* state, const float* grad, int64_t n, float lr, fl
 int repro_adamw(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
                 float weight_decay, int64_t step, void* stream) {
   return repro_adamw_variant(state, grad, n, lr, beta1, beta2, eps, weight_decay, step, 0, stream);
+}
+
+namespace {
+
+// A second stream per device and a pool of events, created on first use and
+// kept for the life of the process, for the AdamW / hash pipeline.  The whole
+// enqueue sequence of a call runs under one lock, so concurrent callers on
+// one device never interleave their event records.
+struct SideStream {
+  hipStream_t stream[2] = {nullptr, nullptr};
+  std::vector<hipEvent_t> events;
+};
+constexpr int kMaxDevices = 64;
+std::mutex g_side_mutex;
+SideStream g_side[kMaxDevices];
+
+hipError_t side_stream(int device, size_t nevents, SideStream** out) {
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  SideStream& r = g_side[device];
+  for (hipStream_t& st : r.stream) {
+    if (st == nullptr) {
+      const hipError_t e = hipStreamCreateWithFlags(&st, hipStreamNonBlocking);
+      if (e != hipSuccess) return e;
+    }
+  }
+  while (r.events.size() < nevents) {
+    hipEvent_t ev;
+    const hipError_t e = hipEventCreateWithFlags(&ev, hipEventDisableTiming);
+    if (e != hipSuccess) return e;
+    r.events.push_back(ev);
+  }
+  *out = &r;
+  return hipSuccess;
+}
+
+constexpr int64_t kLeafWords = 1024;            // a 4096-byte hash leaf
+// 2^26 elements per chunk: 196,608 leaves per hash launch (768 workgroups),
+// the fastest of 2^23 .. 2^28 measured on the optimizer workload.
+constexpr int64_t kDefaultChunk = int64_t(1) << 26;
+
+}  // namespace
+
+int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, int64_t step, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
+                     int64_t chunk, void* stream) {
+  if (n < 0 || step < 1 || workspace == nullptr || digest_out == nullptr) return REPRO_EINVAL;
+  if (chunk > 0 && chunk % kLeafWords != 0) return REPRO_EINVAL;
+  if (n > 0 && (state == nullptr || grad == nullptr)) return REPRO_EINVAL;
+  if (n > 0 && (!aligned4(state) || !aligned4(grad))) return REPRO_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 || (reinterpret_cast<uintptr_t>(digest_out) & 15u) != 0)
+    return REPRO_EALIGN;
+  repro::HashPlan plan;
+  repro::plan_state_hash(3 * n, &plan);
+  if (ws_bytes < plan.total_bytes) return REPRO_ESPACE;
+  uint8_t* ws = static_cast<uint8_t*>(workspace);
+  const hipStream_t main = static_cast<hipStream_t>(stream);
+  const AdamwScalars s = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step);
+  if (chunk == 0) chunk = kDefaultChunk;
+  // Without whole leaves per region (or asked not to), the two run in turn.
+  if (chunk < 0 || n % kLeafWords != 0 || n <= chunk) {
+    if (n > 0) {
+      const hipError_t e = repro::launch_adamw(state, grad, n, s, 0, main);
+      if (e != hipSuccess) return status_of(e);
+    }
+    return status_of(repro::launch_state_hash(state, 3 * n, ws, plan, digest_out, main));
+  }
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return status_of(e);
+  const int64_t nchunks = (n + chunk - 1) / chunk;
+  std::lock_guard<std::mutex> lock(g_side_mutex);
+  SideStream* side = nullptr;
+  e = side_stream(device, (size_t)nchunks + 3, &side);
+  if (e != hipSuccess) return status_of(e);
+  // Fork: the side streams start after everything already on the caller's.
+  if ((e = hipEventRecord(side->events[0], main)) != hipSuccess) return status_of(e);
+  for (hipStream_t st : side->stream)
+    if ((e = hipStreamWaitEvent(st, side->events[0], 0)) != hipSuccess) return status_of(e);
+  const int64_t leaves_per_region = n / kLeafWords;
+  for (int64_t c = 0; c < nchunks; ++c) {
+    const int64_t first = c * chunk;
+    const int64_t count = n - first < chunk ? n - first : chunk;
+    e = repro::launch_adamw_ptrs(state + first, state + n + first, state + 2 * n + first, grad + first, count, s, 0,
+                                 main);
+    if (e != hipSuccess) return status_of(e);
+    hipEvent_t done = side->events[(size_t)c + 1];
+    if ((e = hipEventRecord(done, main)) != hipSuccess) return status_of(e);
+    // This chunk's leaves in w, m and v, in one launch; chunks alternate
+    // between the two side streams so one launch's tail overlaps the next.
+    hipStream_t hs = side->stream[c & 1];
+    if ((e = hipStreamWaitEvent(hs, done, 0)) != hipSuccess) return status_of(e);
+    e = repro::launch_hash_leaves(state, 3 * n, ws, plan, first / kLeafWords, count / kLeafWords, leaves_per_region,
+                                  3, hs);
+    if (e != hipSuccess) return status_of(e);
+  }
+  // Join, then the levels above the leaves on the caller's stream.
+  for (int k = 0; k < 2; ++k) {
+    hipEvent_t joined = side->events[(size_t)nchunks + 1 + k];
+    if ((e = hipEventRecord(joined, side->stream[k])) != hipSuccess) return status_of(e);
+    if ((e = hipStreamWaitEvent(main, joined, 0)) != hipSuccess) return status_of(e);
+  }
+  return status_of(repro::launch_hash_upper(ws, plan, digest_out, main));
 }
 
 int64_t repro_state_hash_workspace_bytes(int64_t n_words) {

@@ -233,9 +233,11 @@ hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* 
 
 hipError_t launch_adamw(float* state, const float* grad, int64_t n, const AdamwScalars& s, int variant,
                         hipStream_t stream) {
-  float* w = state;
-  float* m = state + n;
-  float* v = state + 2 * n;
+  return launch_adamw_ptrs(state, state + n, state + 2 * n, grad, n, s, variant, stream);
+}
+
+hipError_t launch_adamw_ptrs(float* w, float* m, float* v, const float* grad, int64_t n, const AdamwScalars& s,
+                             int variant, hipStream_t stream) {
   const bool vec = variant != 1 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(grad);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {

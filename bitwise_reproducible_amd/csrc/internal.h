@@ -36,6 +36,9 @@ hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* 
                               int variant, hipStream_t stream);
 hipError_t launch_adamw(float* state, const float* grad, int64_t n, const AdamwScalars& s, int variant,
                         hipStream_t stream);
+// The same update on `count` elements of separate w, m, v, g arrays.
+hipError_t launch_adamw_ptrs(float* w, float* m, float* v, const float* grad, int64_t count, const AdamwScalars& s,
+                             int variant, hipStream_t stream);
 hipError_t launch_fp32_ops(int op, const float* a, const float* b, float* out, int64_t n, hipStream_t stream);
 
 // replay.hip
@@ -89,6 +92,11 @@ struct HashPlan {
   int64_t total_bytes;              // workspace bytes needed
 };
 void plan_state_hash(int64_t n_words, HashPlan* plan);
+// Level 0 only: `ranges` runs of `count` leaves at first + r * stride; then
+// the levels above.
+hipError_t launch_hash_leaves(const float* words, int64_t n_words, uint8_t* workspace, const HashPlan& plan,
+                              int64_t first, int64_t count, int64_t stride, int ranges, hipStream_t stream);
+hipError_t launch_hash_upper(uint8_t* workspace, const HashPlan& plan, uint8_t* digest_out, hipStream_t stream);
 hipError_t launch_state_hash(const float* words, int64_t n_words, uint8_t* workspace, const HashPlan& plan,
                              uint8_t* digest_out, hipStream_t stream);
 

@@ -161,11 +161,17 @@ __device__ void hash_words_generic(uint64_t (&h)[8], const uint32_t* __restrict_
 // Level 0.  One lane per leaf.  Full leaves of a 16-byte aligned input take
 // the pipelined path; the last leaf, if short, and unaligned inputs take the
 // word-by-word path.
+// The leaves of `ranges` equal runs of `count` leaves starting at
+// first + r * stride (r = 0 .. ranges-1), of `leaves` in all: one run for a
+// whole level, or the same span of w, m and v after an update chunk.
 template <bool ALIGNED>
 __global__ __launch_bounds__(256) void k_hash_leaves(const float* __restrict__ words, uint64_t nbytes,
-                                                      int64_t leaves, uint8_t* __restrict__ out) {
-  const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
-  if (i >= leaves) return;
+                                                      int64_t leaves, int64_t first, int64_t count, int64_t stride,
+                                                      int ranges, uint8_t* __restrict__ out) {
+  const int64_t k = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
+  if (k >= count * ranges) return;
+  const int64_t r = k / count;
+  const int64_t i = first + r * stride + (k - r * count);
   uint64_t h[8];
   init_node(h, (uint64_t)i, 0);
   const bool last_node = i == leaves - 1;
@@ -272,18 +278,33 @@ void plan_state_hash(int64_t n_words, HashPlan* plan) {
   plan->total_bytes = offset;
 }
 
-hipError_t launch_state_hash(const float* words, int64_t n_words, uint8_t* ws, const HashPlan& plan,
-                             uint8_t* digest_out, hipStream_t stream) {
+hipError_t launch_hash_leaves(const float* words, int64_t n_words, uint8_t* ws, const HashPlan& plan, int64_t first,
+                              int64_t count, int64_t stride, int ranges, hipStream_t stream) {
   const uint64_t nbytes = (uint64_t)n_words * 4u;
   const int64_t leaves = plan.count[0];
+  if (first < 0 || count < 0 || stride < 0 || ranges < 1 || first + (ranges - 1) * stride + count > leaves)
+    return hipErrorInvalidValue;
+  if (count == 0) return hipSuccess;
   const bool aligned = (reinterpret_cast<uintptr_t>(words) & 15u) == 0;
-  const int64_t grid0 = (leaves + 255) / 256;
+  const int64_t grid0 = (count * ranges + 255) / 256;
+  if (grid0 > 0x7fffffff) return hipErrorInvalidValue;
   if (aligned)
     hipLaunchKernelGGL(k_hash_leaves<true>, dim3((unsigned)grid0), dim3(256), 0, stream, words, nbytes, leaves,
-                       ws + plan.offset[0]);
+                       first, count, stride, ranges, ws + plan.offset[0]);
   else
     hipLaunchKernelGGL(k_hash_leaves<false>, dim3((unsigned)grid0), dim3(256), 0, stream, words, nbytes, leaves,
-                       ws + plan.offset[0]);
+                       first, count, stride, ranges, ws + plan.offset[0]);
+  return hipGetLastError();
+}
+
+hipError_t launch_state_hash(const float* words, int64_t n_words, uint8_t* ws, const HashPlan& plan,
+                             uint8_t* digest_out, hipStream_t stream) {
+  const hipError_t e = launch_hash_leaves(words, n_words, ws, plan, 0, plan.count[0], 0, 1, stream);
+  if (e != hipSuccess) return e;
+  return launch_hash_upper(ws, plan, digest_out, stream);
+}
+
+hipError_t launch_hash_upper(uint8_t* ws, const HashPlan& plan, uint8_t* digest_out, hipStream_t stream) {
   int d = 1;
   for (; d < plan.levels && plan.count[d] > kTailNodes; ++d) {
     const int64_t grid = (plan.count[d] + 255) / 256;

@@ -325,6 +325,35 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
                      uint8_t* digest_out, void* stream);
 
 /*
+ * repro_adamw_hash: repro_adamw on the flat state, then repro_state_hash of
+ * the updated [w | m | v] (3n words), with the same results bit for bit.
+ *
+ * Paper section 3.2 (the fused step) and Appendix B with Figure 11 (the
+ * per-step state hash, whose move from the host onto the device the pages
+ * name as their next step).  The update is bound by memory traffic and the
+ * hash by integer arithmetic, so the two are overlapped: the update runs in
+ * chunks of `chunk` elements on the caller's stream, and as each chunk
+ * completes, the hash leaves it covers in w, m and v (chunk / 1024 each) are
+ * hashed on a second stream of the library's; the levels above the leaves
+ * follow on the caller's stream once both are done.
+ *
+ *   state, grad, n, lr ... step: as repro_adamw.
+ *   workspace, ws_bytes: as repro_state_hash for 3n words.
+ *   digest_out: device pointer to 32 bytes (16-byte aligned).
+ *   chunk: elements per chunk, a multiple of 1024; 0 = the library's
+ *          default (2^26); negative = no overlap (update, then hash, both on
+ *          the caller's stream).  When n is not a multiple of 1024 (leaves
+ *          would straddle w, m and v) or n <= chunk the two run in turn.
+ * Asynchronous: the caller's stream is ordered after all of the work.  The
+ * library's second stream and its events are created on the first call on
+ * a device and live until the process ends; each call enqueues under a
+ * lock.
+ */
+int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
+                     float weight_decay, int64_t step, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
+                     int64_t chunk, void* stream);
+
+/*
  * repro_fp32_ops: one contract operation per element, out[i] = a[i] op b[i],
  * in the same device arithmetic the kernels use (a diagnostic entry point for
  * directed tests of the flush rule, division and square root).
