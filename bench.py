@@ -373,7 +373,7 @@ def main():
     next_rows["adamw_bf16_step"] = {
         "workload": f"n={n} bf16 w, fp32 m and v, bf16 g (norm ~3.5, clipped to 1.0), beta2 0.95",
         "ms": round(bf16_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("adamw_bf16_step")}
     for variant, unit in ((0, "matrix cores, v_mfma_f32_32x32x1_2b_f32"), (1, "VALU, v_fma_f32")):
         ms = fma_ms[(variant, "fwd")] + fma_ms[(variant, "dw")]
         ach = (flops_fwd + flops_dw) / (ms * 1e-3) / 1e12
