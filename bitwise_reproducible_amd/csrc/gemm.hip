@@ -489,8 +489,10 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   // chunk is either wholly inside or wholly outside the matrix.
   const int64_t a_contig = trans_a ? M : K;
   const int64_t b_contig = trans_b ? K : N;
-  const bool vec = variant != 1 && al16(A) && al16(B) && lda % 4 == 0 && ldb % 4 == 0 && a_contig % 4 == 0 &&
-                   b_contig % 4 == 0;
+  // (Variant 1 of the unfused kernels forces scalar loads; the fused
+  // variants always take 16-byte loads when they can.)
+  const bool vec = (fused || variant != 1) && al16(A) && al16(B) && lda % 4 == 0 && ldb % 4 == 0 &&
+                   a_contig % 4 == 0 && b_contig % 4 == 0;
   if (fused) {  // variant 0: matrix cores, 1: VALU v_fma_f32
     if (variant == 0)
       return dispatch_mfma<true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);

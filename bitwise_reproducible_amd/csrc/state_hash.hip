@@ -14,8 +14,10 @@
 //  - one lane per 4 KiB leaf (32 compressions), all rounds unrolled so the
 //    message schedule is resolved at compile time and the 16 message words,
 //    the 16 state words and the chaining value stay in VGPRs;
-//  - the next block's eight 16-byte loads are issued before the current
-//    block is compressed, so HBM latency hides behind ALU work;
+//  - each block's eight 16-byte loads are issued right before it is
+//    compressed; at ~100 VGPRs five waves share a SIMD and hide the load
+//    latency (prefetching the next block instead costs 32 more VGPRs, one
+//    wave fewer, and measured 2% slower);
 //  - upper levels with many nodes run one lane per node (a node reads 16
 //    digests = 512 bytes = 4 compressions); the last levels (at most
 //    kTailNodes nodes) run in one workgroup with a barrier between levels,
@@ -180,14 +182,11 @@ __global__ __launch_bounds__(256) void k_hash_leaves(const float* __restrict__ w
   const uint32_t* w = reinterpret_cast<const uint32_t*>(words) + start / 4;
   if (ALIGNED && len == (uint64_t)kLeafBytes) {
     const uint4* p = reinterpret_cast<const uint4*>(w);
-    uint64_t m[16], nx[16];
-    load_block16(m, p);
     for (int b = 0; b < kLeafBytes / 128; ++b) {
-      if (b + 1 < kLeafBytes / 128) load_block16(nx, p + 8 * (b + 1));
+      uint64_t m[16];
+      load_block16(m, p + 8 * b);
       const bool last = b + 1 == kLeafBytes / 128;
       compress(h, m, (uint64_t)(b + 1) * 128, last, last_node);
-#pragma unroll
-      for (int q = 0; q < 16; ++q) m[q] = nx[q];
     }
   } else {
     hash_words_generic(h, w, len, last_node);
