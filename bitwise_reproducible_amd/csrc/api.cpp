@@ -246,8 +246,9 @@ hipError_t side_stream(int device, size_t nevents, SideStream** out) {
 }
 
 constexpr int64_t kLeafWords = 1024;            // a 4096-byte hash leaf
-// 2^26 elements per chunk: 196,608 leaves per hash launch (768 workgroups),
-// the fastest of 2^23 .. 2^28 measured on the optimizer workload.
+// Pipelined form: 2^26 elements per chunk, 196,608 leaves per hash launch
+// (768 workgroups), the fastest of 2^23 .. 2^28 measured on the optimizer
+// workload.
 constexpr int64_t kDefaultChunk = int64_t(1) << 26;
 
 }  // namespace
@@ -267,6 +268,9 @@ int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float
   uint8_t* ws = static_cast<uint8_t*>(workspace);
   const hipStream_t main = static_cast<hipStream_t>(stream);
   const AdamwScalars s = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step);
+  const bool al16 = ((reinterpret_cast<uintptr_t>(state) | reinterpret_cast<uintptr_t>(grad)) & 15u) == 0;
+  if (chunk == 0 && n > 0 && n % kLeafWords == 0 && al16)
+    return status_of(repro::launch_adamw_hash_fused(state, grad, n, s, ws, plan, digest_out, main));
   if (chunk == 0) chunk = kDefaultChunk;
   // Without whole leaves per region (or asked not to), the two run in turn.
   if (chunk < 0 || n % kLeafWords != 0 || n <= chunk) {

@@ -97,6 +97,10 @@ void plan_state_hash(int64_t n_words, HashPlan* plan);
 hipError_t launch_hash_leaves(const float* words, int64_t n_words, uint8_t* workspace, const HashPlan& plan,
                               int64_t first, int64_t count, int64_t stride, int ranges, hipStream_t stream);
 hipError_t launch_hash_upper(uint8_t* workspace, const HashPlan& plan, uint8_t* digest_out, hipStream_t stream);
+// AdamW on [w | m | v] and the whole state hash, the update and the leaf
+// level in one kernel (n a multiple of 1024, state and grad 16-byte aligned).
+hipError_t launch_adamw_hash_fused(float* state, const float* grad, int64_t n, const AdamwScalars& s, uint8_t* ws,
+                                   const HashPlan& plan, uint8_t* digest_out, hipStream_t stream);
 hipError_t launch_state_hash(const float* words, int64_t n_words, uint8_t* workspace, const HashPlan& plan,
                              uint8_t* digest_out, hipStream_t stream);
 

@@ -331,23 +331,27 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
  * Paper section 3.2 (the fused step) and Appendix B with Figure 11 (the
  * per-step state hash, whose move from the host onto the device the pages
  * name as their next step).  The update is bound by memory traffic and the
- * hash by integer arithmetic, so the two are overlapped: the update runs in
- * chunks of `chunk` elements on the caller's stream, and as each chunk
- * completes, the hash leaves it covers in w, m and v (chunk / 1024 each) are
- * hashed on a second stream of the library's; the levels above the leaves
- * follow on the caller's stream once both are done.
+ * hash by integer arithmetic, so they are not run one after the other:
+ *   chunk == 0 (default): one kernel updates each 128-byte block of every
+ *          leaf and hashes it from on-chip memory right away, so the
+ *          updated state is written once and never read back; the levels
+ *          above the leaves follow.  Needs n a multiple of 1024 (so no leaf
+ *          straddles w, m and v) and 16-byte aligned state and grad;
+ *          otherwise the call proceeds as for chunk == 2^26.
+ *   chunk > 0: a multiple of 1024; the update runs in chunks of `chunk`
+ *          elements on the caller's stream, and as each chunk completes the
+ *          leaves it covers in w, m and v are hashed on a second stream of
+ *          the library's (when n is not a multiple of 1024, or n <= chunk,
+ *          the two run in turn);
+ *   chunk < 0: the update, then the hash, both on the caller's stream.
  *
  *   state, grad, n, lr ... step: as repro_adamw.
  *   workspace, ws_bytes: as repro_state_hash for 3n words.
  *   digest_out: device pointer to 32 bytes (16-byte aligned).
- *   chunk: elements per chunk, a multiple of 1024; 0 = the library's
- *          default (2^26); negative = no overlap (update, then hash, both on
- *          the caller's stream).  When n is not a multiple of 1024 (leaves
- *          would straddle w, m and v) or n <= chunk the two run in turn.
- * Asynchronous: the caller's stream is ordered after all of the work.  The
- * library's second stream and its events are created on the first call on
- * a device and live until the process ends; each call enqueues under a
- * lock.
+ * Asynchronous: the caller's stream is ordered after all of the work.  For
+ * chunk > 0 the library's second streams and their events are created on
+ * the first such call on a device and live until the process ends; each
+ * call enqueues under a lock.
  */
 int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
                      float weight_decay, int64_t step, void* workspace, int64_t ws_bytes, uint8_t* digest_out,

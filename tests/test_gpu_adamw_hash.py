@@ -26,8 +26,12 @@ def _state(n, seed):
     return np.concatenate([w, m, v]), g
 
 
+# chunk 0 with n a multiple of 1024: the single fused kernel (64 leaf
+# triples per workgroup; 197 * 1024 leaves a partial last workgroup);
+# chunk > 0: the two-stream pipeline; chunk < 0 or short n: in turn.
 @pytest.mark.parametrize("n,chunk", [(5000, 0), (37 * 1024, 5 * 1024), (37 * 1024, 1024), (37 * 1024, -1),
-                                     (64 * 1024, 16 * 1024), (3 * 1024, 0), (1024, 1024)])
+                                     (64 * 1024, 16 * 1024), (3 * 1024, 0), (1024, 1024), (1024, 0),
+                                     (37 * 1024, 0), (197 * 1024, 0), (128 * 1024, 0)])
 def test_matches_oracle(n, chunk):
     st, g = _state(n, 16 + n % 7)
     ref = st.copy()
@@ -41,7 +45,23 @@ def test_matches_oracle(n, chunk):
     assert bytes(digest.cpu().numpy().tobytes()) == ref_digest
 
 
-def test_steps_equal_the_two_calls_in_turn():
+def test_unaligned_view_takes_the_pipeline():
+    n = 40 * 1024
+    st, g = _state(n, 60)
+    ref = st.copy()
+    oracle.adamw_inplace(ref, g, step=2, **HP)
+    big = to_dev(np.concatenate([[0], st]).astype(np.float32))
+    dst = big[1:]  # 4-byte aligned only
+    dg = to_dev(g)
+    ws = br.hash_workspace(3 * n)
+    digest = torch.empty(32, dtype=torch.uint8, device="cuda")
+    br.repro_adamw_hash(dst, dg, digest, ws, step=2, **HP)
+    assert_bitwise(to_host(dst), ref, "unaligned state")
+    assert bytes(digest.cpu().numpy().tobytes()) == oracle.state_hash(ref)
+
+
+@pytest.mark.parametrize("chunk", [0, 8 * 1024])
+def test_steps_equal_the_two_calls_in_turn(chunk):
     n = 48 * 1024
     st, g = _state(n, 40)
     a, b = to_dev(st), to_dev(st)
@@ -50,7 +70,7 @@ def test_steps_equal_the_two_calls_in_turn():
     da = torch.empty(32, dtype=torch.uint8, device="cuda")
     db = torch.empty(32, dtype=torch.uint8, device="cuda")
     for step in range(1, 6):
-        br.repro_adamw_hash(a, dg, da, wa, step=step, chunk=8 * 1024, **HP)
+        br.repro_adamw_hash(a, dg, da, wa, step=step, chunk=chunk, **HP)
         br.repro_adamw(b, dg, step=step, **HP)
         br.repro_state_hash_async(b, db, wb)
         assert torch.equal(a.view(torch.int32), b.view(torch.int32))
@@ -83,7 +103,8 @@ def test_other_stream_and_errors():
 
 
 def test_full_size_equals_the_two_calls():
-    # The optimizer workload (n = 1.2e9, [w|m|v] 14.4 GB), default chunk.
+    # The optimizer workload (n = 1.2e9, [w|m|v] 14.4 GB), fused kernel, and
+    # the pipelined form on a third copy.
     AC = synth.ADAMW
     n = AC["n"]
     print(f"adamw+hash n={n}", flush=True)
@@ -92,12 +113,18 @@ def test_full_size_equals_the_two_calls():
         st[k * n:(k + 1) * n].copy_(torch.from_numpy(gen()))
     g = torch.from_numpy(synth.adamw_g()).cuda()
     other = st.clone()
+    third = st.clone()
     ws = br.hash_workspace(3 * n)
     d1 = torch.empty(32, dtype=torch.uint8, device="cuda")
     d2 = torch.empty(32, dtype=torch.uint8, device="cuda")
+    d3 = torch.empty(32, dtype=torch.uint8, device="cuda")
     hp = dict(lr=AC["lr"], beta1=AC["beta1"], beta2=AC["beta2"], eps=AC["eps"], weight_decay=AC["wd"])
     br.repro_adamw_hash(st, g, d1, ws, step=AC["step"], **hp)
     br.repro_adamw(other, g, step=AC["step"], **hp)
     br.repro_state_hash_async(other, d2, ws)
     assert torch.equal(st.view(torch.int32), other.view(torch.int32))
     assert torch.equal(d1, d2)
+    del other
+    br.repro_adamw_hash(third, g, d3, ws, step=AC["step"], chunk=1 << 26, **hp)
+    assert torch.equal(st.view(torch.int32), third.view(torch.int32))
+    assert torch.equal(d1, d3)
