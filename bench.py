@@ -5,23 +5,24 @@ One step is one pass of the whole hot path over the full synthetic workloads,
 every input already resident in HBM:
   1. repro_tree_reduce   R = 8 replicas x 16,777,216 floats, x fl(1/8)
   2. repro_gemm          Y[8192x8192] = X[8192x2048] W[2048x8192]
-  3. repro_adamw         flat [w|m|v] of n = 1.2e9, grad n (step counter advances)
-  4. repro_state_hash    BLAKE2b tree over the 14.4 GB [w|m|v]
-  5. repro_gemm          dW[2048x8192] = X^T dY, X[16384x2048], dY[16384x8192]
-Each op is bracketed by HIP events on the stream it runs on.  After the
-steps, the audit replay of one step's reduction (OPEN-1B section 6,
-Algorithm 1: 6 replicas x 8 shards x 6 microbatches over an 8,388,608-float
-slice, repro_replay_reduce) and the fused multiply-add GEMM convention
-(repro_gemm_fma on both GEMM workloads, matrix cores and VALU), AdamW with
-the state hash overlapped (repro_adamw_hash) and the BF16-parameter
-optimizer step (repro_adamw_bf16_step: norm, clip, update on
-n = 1.2e9) are timed on their own and reported under "next_rows"; they are
-not part of the step.  `value` is the
-GB/s of the memory-side ops (1, 3, 4: algorithmic bytes over their summed
-event time); the GEMMs are reported in GFLOP/s beside it.  After the timed
-steps the outputs are checked against the CPU oracle (every word of the
-reduce output, sampled rows and columns of both GEMMs, sampled AdamW
-elements replayed through every step, sampled hash leaves), and the oracle
+  3. repro_adamw_hash    the AdamW update of the flat [w|m|v] (n = 1.2e9, step
+                         counter advancing) and the BLAKE2b tree hash of the
+                         updated 14.4 GB, in one kernel that hashes each block
+                         as it is written
+  4. repro_gemm          dW[2048x8192] = X^T dY, X[16384x2048], dY[16384x8192]
+Each op is bracketed by HIP events on the stream it runs on.  `value` is the
+GB/s of the memory-side work (reduce bytes, AdamW bytes and the hashed bytes
+over the event time of ops 1 and 3); the GEMMs are reported in GFLOP/s
+beside it.  After the steps, and not part of them: repro_adamw and
+repro_state_hash as separate calls ("ops_in_turn", each kernel's own
+roofline), and under "next_rows" the audit replay of one step's reduction
+(OPEN-1B section 6, Algorithm 1: 6 replicas x 8 shards x 6 microbatches over
+an 8,388,608-float slice), the fused multiply-add GEMM convention
+(repro_gemm_fma, matrix cores and VALU) and the BF16-parameter optimizer
+step (norm, clip, update on n = 1.2e9).  Then the outputs are checked
+against the CPU oracle (every word of the reduce output, sampled rows and
+columns of the GEMMs, sampled AdamW elements replayed through every step,
+sampled hash leaves, the replay and BF16 step on samples), and the oracle
 itself is timed on a bounded sample as the CPU baseline.
 
 Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
@@ -53,6 +54,10 @@ GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
 # xors of the feed-forward: 3088 slots per 128 bytes.
 HASH_SLOTS_PER_BYTE = (12 * 8 * 32 + 16) / 128
 HASH_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
+# The AdamW update: 170 VALU instructions per four elements in the compiled
+# kernel (16 operations each, with the correctly rounded division and square
+# root sequences), about 42 issue slots per element.
+ADAMW_SLOTS_PER_ELEMENT = 42
 
 
 def recorded_traffic():
@@ -220,7 +225,7 @@ def main():
     log(f"inputs resident in HBM after {time.time() - t_setup:.1f} s")
 
     hp = dict(lr=AC["lr"], beta1=AC["beta1"], beta2=AC["beta2"], eps=AC["eps"], weight_decay=AC["wd"])
-    ops = ["tree_reduce", "gemm_fwd", "adamw", "state_hash", "gemm_dw"]
+    ops = ["tree_reduce", "gemm_fwd", "adamw_state_hash", "gemm_dw"]
     step_counter = [AC["step"]]
 
     def one_step(events=None):
@@ -230,18 +235,16 @@ def main():
         rec(1)
         br.repro_gemm(X3, W3, out=Y3)
         rec(2)
-        br.repro_adamw(state, grad, step=step_counter[0], **hp)
+        br.repro_adamw_hash(state, grad, digest, ws, step=step_counter[0], **hp)  # update + hash, one kernel
         step_counter[0] += 1
         rec(3)
-        br.repro_state_hash_async(state, digest, ws)
-        rec(4)
         br.repro_gemm(X5, dY5, trans_a=True, out=dW5)
-        rec(5)
+        rec(4)
 
     for _ in range(args.warmup):
         one_step()
     torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(6)] for _ in range(args.steps)]
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(ops) + 1)] for _ in range(args.steps)]
     torch.cuda.synchronize()
     t0 = time.perf_counter()
     for s in range(args.steps):
@@ -284,24 +287,29 @@ def main():
             fma_ms[(variant, name)] = float(np.mean([f_evs[i].elapsed_time(f_evs[i + 1])
                                                      for i in range(args.steps)]))
 
-    # AdamW and the state hash overlapped (repro_adamw_hash), on a copy of
-    # the optimizer state that continues from the steps' last step counter.
+    # AdamW, then the state hash, as separate calls (repro_adamw,
+    # repro_state_hash), for each kernel's own roofline: on a copy of the
+    # optimizer state that continues from the steps' last step counter.
     state2 = state.clone()
     ws2 = br.hash_workspace(3 * n, dev)  # the steps' leaf digests in ws are checked later
     digest2 = torch.empty(32, dtype=torch.uint8, device=dev)
     ah_step0 = step_counter[0]
     for _ in range(args.warmup):
-        br.repro_adamw_hash(state2, grad, digest2, ws2, step=step_counter[0], **hp)
+        br.repro_adamw(state2, grad, step=step_counter[0], **hp)
+        br.repro_state_hash_async(state2, digest2, ws2)
         step_counter[0] += 1
-    ah_evs = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
+    ah_evs = [[torch.cuda.Event(enable_timing=True) for _ in range(3)] for _ in range(args.steps)]
     torch.cuda.synchronize()
-    ah_evs[0].record()
     for s_ in range(args.steps):
-        br.repro_adamw_hash(state2, grad, digest2, ws2, step=step_counter[0], **hp)
+        ah_evs[s_][0].record()
+        br.repro_adamw(state2, grad, step=step_counter[0], **hp)
         step_counter[0] += 1
-        ah_evs[s_ + 1].record()
+        ah_evs[s_][1].record()
+        br.repro_state_hash_async(state2, digest2, ws2)
+        ah_evs[s_][2].record()
     torch.cuda.synchronize()
-    ah_ms = float(np.mean([ah_evs[i].elapsed_time(ah_evs[i + 1]) for i in range(args.steps)]))
+    turn_ms = {"adamw": float(np.mean([e[0].elapsed_time(e[1]) for e in ah_evs])),
+               "state_hash": float(np.mean([e[1].elapsed_time(e[2]) for e in ah_evs]))}
 
     # The BF16 optimizer step, timed on its own.
     bhp = dict(lr=AC["lr"], beta1=0.9, beta2=0.95, eps=AC["eps"], weight_decay=AC["wd"], max_norm=1.0,
@@ -327,19 +335,29 @@ def main():
     bytes_hash = 12 * n
     flops_fwd = 2 * GC["M"] * GC["N"] * GC["K"]
     flops_dw = 2 * DC["M"] * DC["N"] * DC["K"]
-    mem_ms = op_ms["tree_reduce"] + op_ms["adamw"] + op_ms["state_hash"]
+    mem_ms = op_ms["tree_reduce"] + op_ms["adamw_state_hash"]
     value = (bytes_reduce + bytes_adamw + bytes_hash) / (mem_ms * 1e-3) / 1e9
     gemm_ms = op_ms["gemm_fwd"] + op_ms["gemm_dw"]
     gemm_gflops = (flops_fwd + flops_dw) / (gemm_ms * 1e-3) / 1e9
 
-    def roof(op):
-        ms = op_ms[op]
+    def roof(op, ms):
         if op in ("gemm_fwd", "gemm_dw"):
             f = flops_fwd if op == "gemm_fwd" else flops_dw
             ach = f / (ms * 1e-3) / 1e12
             return {"bound": "alu", "achieved": round(ach, 3), "peak": round(GEMM_PEAK_TFLOPS, 2),
                     "unit": "TFLOP/s", "frac": round(ach / GEMM_PEAK_TFLOPS, 4), "traffic": None,
                     "frac_of_fp32_vector_peak": round(ach / FP32_VECTOR_PEAK, 4)}
+        if op == "adamw_state_hash":
+            # One kernel, bound by the tighter of HBM (28n bytes) and the
+            # VALU issue of the hash plus the update (slots per element).
+            t_hbm = bytes_adamw / (HBM_PEAK_GBS * 1e9)
+            t_alu = n * (12 * HASH_SLOTS_PER_BYTE + ADAMW_SLOTS_PER_ELEMENT) / VALU_LANE_OPS
+            peak = bytes_hash / max(t_hbm, t_alu) / 1e9
+            ach = bytes_hash / (ms * 1e-3) / 1e9
+            return {"bound": "alu" if t_alu >= t_hbm else "hbm", "achieved": round(ach, 1), "peak": round(peak, 1),
+                    "unit": "GB/s (of state hashed)", "frac": round(ach / peak, 4), "traffic": None,
+                    "hbm_achieved": round(bytes_adamw / (ms * 1e-3) / 1e9, 1),
+                    "frac_of_hbm_peak": round(bytes_adamw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
         b = {"tree_reduce": bytes_reduce, "adamw": bytes_adamw, "state_hash": bytes_hash}[op]
         ach = b / (ms * 1e-3) / 1e9
         if op == "state_hash":  # integer-VALU bound: ~24 issue slots per byte
@@ -349,11 +367,13 @@ def main():
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
 
-    per_op = {op: {"ms": round(op_ms[op], 4), **roof(op)} for op in ops}
+    per_op = {op: {"ms": round(op_ms[op], 4), **roof(op, op_ms[op])} for op in ops}
+    in_turn = {op: {"ms": round(turn_ms[op], 4), **roof(op, turn_ms[op])} for op in ("adamw", "state_hash")}
     traffic = recorded_traffic()
     for op in ops:
-        key = "state_hash_leaves" if op == "state_hash" else op
-        per_op[op]["traffic"] = traffic.get(key)
+        per_op[op]["traffic"] = traffic.get(op)
+    for op in in_turn:
+        in_turn[op]["traffic"] = traffic.get("state_hash_leaves" if op == "state_hash" else op)
     dominant = max(ops, key=lambda o: op_ms[o])
     bytes_replay = (p_nbuf + 1) * 4 * PC["n"]
     ach = bytes_replay / (replay_ms * 1e-3) / 1e9
@@ -362,12 +382,6 @@ def main():
                     f"({p_nbuf} buffers) n={PC['n']}",
         "ms": round(replay_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
         "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce")}}
-    ach = (bytes_adamw + bytes_hash) / (ah_ms * 1e-3) / 1e9
-    next_rows["adamw_hash_overlapped"] = {
-        "workload": "the adamw + state_hash workload in one call, update chunks of 2^26 elements overlapped with "
-                    "the hash of the chunk before on a second stream",
-        "ms": round(ah_ms, 4), "ms_in_turn": round(op_ms["adamw"] + op_ms["state_hash"], 4),
-        "achieved": round(ach, 1), "unit": "GB/s", "bytes": bytes_adamw + bytes_hash}
     bytes_bf16 = 24 * n  # norm pass reads g (2n); update reads w, m, v, g (12n), writes w, m, v (10n)
     ach = bytes_bf16 / (bf16_ms * 1e-3) / 1e9
     next_rows["adamw_bf16_step"] = {
@@ -391,6 +405,7 @@ def main():
                    "parallelism": "none (1 GPU)"},
         "gemm": {"value": round(gemm_gflops, 1), "unit": "GFLOP/s"},
         "ops": per_op,
+        "ops_in_turn": in_turn,
         "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if k != "ms"}},
         "next_rows": next_rows,
     }
@@ -400,8 +415,8 @@ def main():
                                  (s_w, s_m, s_v, s_g), hp, AC["step"], args.warmup + args.steps)
         out["verified"].update(verify_replay(np, p_out, p_layout, PC["n"]))
         out["verified"].update(verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f))
-        out["verified"].update(verify_adamw_hash(np, torch, br, state2, digest2, ws2, n, aidx, (s_w, s_m, s_v, s_g),
-                                                 hp, AC["step"], ah_step0, step_counter[0]))
+        out["verified"].update(verify_in_turn(np, torch, br, state2, digest2, ws2, n, aidx, (s_w, s_m, s_v, s_g),
+                                              hp, AC["step"], step_counter[0]))
         out["verified"].update(verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, bidx, b_samples, bhp,
                                            args.warmup + args.steps))
     if not args.no_cpu_baseline:
@@ -507,24 +522,25 @@ def verify_fused(np, X3, W3, Y3f, X5, dY5, dW5f):
     return {"gemm_fma_sampled_words_differing": bad, "gemm_fma_seconds": round(time.time() - t, 1)}
 
 
-def verify_adamw_hash(np, torch, br, state2, digest2, ws, n, aidx, samples, hp, step0, ah_step0, ah_end):
-    """The overlapped calls: every AdamW step of the run replayed by the
-    oracle on the sampled elements (the steps', then the overlapped calls'),
-    and the last digest against a separate hash of the final state."""
+def verify_in_turn(np, torch, br, state2, digest2, ws, n, aidx, samples, hp, step0, ah_end):
+    """The copy updated by the separate calls: every AdamW step of the run
+    replayed by the oracle on the sampled elements (the steps', then the
+    separate calls'), and the last digest against a fresh hash of the final
+    state."""
     import oracle
     t = time.time()
     s_w, s_m, s_v, s_g = samples
     st = np.concatenate([s_w, s_m, s_v]).astype(np.float32)
-    for t_ in range(step0, ah_end):  # the steps' updates (to ah_step0), then the overlapped calls'
+    for t_ in range(step0, ah_end):  # the steps' updates, then the separate calls'
         oracle.adamw_inplace(st, s_g, hp["lr"], hp["beta1"], hp["beta2"], hp["eps"], hp["weight_decay"], t_)
     tidx = torch.from_numpy(aidx).to(state2.device)
     got = np.concatenate([state2[:n][tidx].cpu().numpy(), state2[n:2 * n][tidx].cpu().numpy(),
                           state2[2 * n:][tidx].cpu().numpy()])
     d = torch.empty(32, dtype=torch.uint8, device=state2.device)
     br.repro_state_hash_async(state2, d, ws)
-    return {"adamw_hash_sampled_words_differing": int(np.count_nonzero(got.view(np.uint32) != st.view(np.uint32))),
-            "adamw_hash_digest_matches": bool(torch.equal(d, digest2)),
-            "adamw_hash_seconds": round(time.time() - t, 1)}
+    return {"in_turn_adamw_sampled_words_differing": int(np.count_nonzero(got.view(np.uint32) != st.view(np.uint32))),
+            "in_turn_digest_repeats": bool(torch.equal(d, digest2)),
+            "in_turn_seconds": round(time.time() - t, 1)}
 
 
 def verify_bf16(np, torch, br, b_g, b_w, b_m, b_v, b_state, idx, samples, bhp, nsteps):
