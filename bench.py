@@ -252,8 +252,8 @@ def main():
     torch.cuda.synchronize()
     t1 = time.perf_counter()
     ms_per_step = (t1 - t0) * 1e3 / args.steps
-    op_ms = {op: float(np.mean([evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)]))
-             for i, op in enumerate(ops)}
+    op_samples = {op: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, op in enumerate(ops)}
+    op_ms = {op: float(np.mean(v)) for op, v in op_samples.items()}
 
     # The replay, timed on its own: same warmup and count as the steps.
     for _ in range(args.warmup):
@@ -367,7 +367,8 @@ def main():
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
 
-    per_op = {op: {"ms": round(op_ms[op], 4), **roof(op, op_ms[op])} for op in ops}
+    per_op = {op: {"ms": round(op_ms[op], 4), "ms_median": round(float(np.median(op_samples[op])), 4),
+                   "ms_min": round(float(np.min(op_samples[op])), 4), **roof(op, op_ms[op])} for op in ops}
     in_turn = {op: {"ms": round(turn_ms[op], 4), **roof(op, turn_ms[op])} for op in ("adamw", "state_hash")}
     traffic = recorded_traffic()
     for op in ops:
@@ -406,7 +407,7 @@ def main():
         "gemm": {"value": round(gemm_gflops, 1), "unit": "GFLOP/s"},
         "ops": per_op,
         "ops_in_turn": in_turn,
-        "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if k != "ms"}},
+        "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if not k.startswith("ms")}},
         "next_rows": next_rows,
     }
 

@@ -1,8 +1,10 @@
 """Child process for the cross-process determinism test.
 
-Runs the tiny chained workload (GEMM, TreeFold, AdamW, state hash) and the
-full gradient-reduction workload ten times each in a fresh process and prints
-one JSON line of SHA-256 digests of the output words.
+Runs the tiny chained workload (GEMM, TreeFold, AdamW, state hash), the full
+gradient-reduction workload, and small cases of the audit replay, the fused
+GEMM convention (both units), the fused AdamW + hash and the BF16 optimizer
+step, ten times each in a fresh process, and prints one JSON line of SHA-256
+digests of the output words.
 """
 import hashlib
 import json
@@ -23,6 +25,38 @@ def sha(t) -> str:
     return hashlib.sha256(t.detach().cpu().numpy().tobytes()).hexdigest()
 
 
+REPLAY_LAYOUT = (3, 2, 2)
+AH_HP = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=5)
+BF16_HP = dict(lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1, max_norm=1.0, spike_threshold=5.0,
+               skip_steps=5)
+
+
+def replay_inputs():
+    return [synth.generate(4099, synth.OUTLIER_SCALED, synth.tid(9, b), 1e-3, 0.01, 1e4) for b in range(12)]
+
+
+def adamw_hash_inputs():
+    n = 64 * 1024
+    st = np.concatenate([synth.generate(n, synth.NORMAL, synth.tid(9, 0x20), 0.02),
+                         synth.generate(n, synth.NORMAL, synth.tid(9, 0x21), 1e-4),
+                         synth.generate(n, synth.HALF_NORMAL, synth.tid(9, 0x22), 1e-6)])
+    return st, synth.generate(n, synth.NORMAL, synth.tid(9, 0x23), 1e-3)
+
+
+def _bf16_bits(x):
+    return torch.from_numpy(np.ascontiguousarray(x, np.float32)).to(torch.bfloat16).view(torch.int16).numpy().view(
+        np.uint16)
+
+
+def bf16_inputs():
+    n = 5003
+    w = _bf16_bits(synth.generate(n, synth.NORMAL, synth.tid(9, 0x30), 0.02))
+    m = synth.generate(n, synth.NORMAL, synth.tid(9, 0x31), 1e-4)
+    v = synth.generate(n, synth.HALF_NORMAL, synth.tid(9, 0x32), 1e-6)
+    g = _bf16_bits(synth.generate(n, synth.NORMAL, synth.tid(9, 0x33), 0.03))  # norm ~2: clipped
+    return w, m, v, g
+
+
 def main():
     dev = torch.device("cuda:0")
     cfg = synth.TINY
@@ -34,13 +68,34 @@ def main():
     state0 = torch.from_numpy(np.concatenate([synth.tiny_adamw_weights(n), np.zeros(2 * n, np.float32)])).to(dev)
     hp = (cfg["lr"], cfg["beta1"], cfg["beta2"], cfg["eps"], cfg["wd"], cfg["step"])
     big = [torch.from_numpy(synth.reduce_replica(r)).to(dev) for r in range(synth.REDUCE["R"])]
+    grads = [torch.from_numpy(x).to(dev) for x in replay_inputs()]
+    ah_state0, ah_g = (torch.from_numpy(x).to(dev) for x in adamw_hash_inputs())
+    ah_ws = br.hash_workspace(ah_state0.numel())
+    w0, m0, v0, gb = bf16_inputs()
     runs = []
     for _ in range(10):
         g = br.repro_tree_reduce(reps)
         st = state0.clone()
         br.repro_adamw(st, g, *hp)
-        runs.append({"gemm": sha(br.repro_gemm(da, db)), "reduce": sha(g), "adamw": sha(st),
-                     "state_hash": br.repro_state_hash(st).hex(), "reduce_workload": sha(br.repro_tree_reduce(big))})
+        r = {"gemm": sha(br.repro_gemm(da, db)), "reduce": sha(g), "adamw": sha(st),
+             "state_hash": br.repro_state_hash(st).hex(), "reduce_workload": sha(br.repro_tree_reduce(big)),
+             "replay": sha(br.repro_replay_reduce(grads, *REPLAY_LAYOUT)),
+             "gemm_fma0": sha(br.repro_gemm_fma(da, db, variant=0)),
+             "gemm_fma1": sha(br.repro_gemm_fma(da, db, variant=1))}
+        ah = ah_state0.clone()
+        dg = torch.empty(32, dtype=torch.uint8, device=dev)
+        br.repro_adamw_hash(ah, ah_g, dg, ah_ws, **AH_HP)
+        r["adamw_hash_state"] = sha(ah)
+        r["adamw_hash_digest"] = bytes(dg.cpu().numpy()).hex()
+        w = torch.from_numpy(w0.view(np.int16)).to(dev).view(torch.bfloat16)
+        m, v = torch.from_numpy(m0).to(dev), torch.from_numpy(v0).to(dev)
+        gdev = torch.from_numpy(gb.view(np.int16)).to(dev).view(torch.bfloat16)
+        sdev = br.new_step_state(dev)
+        for _k in range(3):
+            br.repro_adamw_bf16_step(w, m, v, gdev, sdev, **BF16_HP)
+        r["bf16_w"] = sha(w.view(torch.int16))
+        r["bf16_m"] = sha(m)
+        runs.append(r)
     out["runs"] = runs
     print(json.dumps(out), flush=True)
 

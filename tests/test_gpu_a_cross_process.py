@@ -56,3 +56,20 @@ def test_two_processes_ten_runs_each_agree_with_the_oracle():
     assert runs[0]["state_hash"] == oracle.state_hash(st).hex()
     big = [synth.reduce_replica(r) for r in range(synth.REDUCE["R"])]
     assert runs[0]["reduce_workload"] == _sha(oracle.tree_reduce(big))
+    # The widened rows: replay, fused GEMM convention, fused AdamW + hash, BF16 step.
+    import cross_process_child as C
+    assert runs[0]["replay"] == _sha(oracle.replay_reduce(C.replay_inputs(), *C.REPLAY_LAYOUT))
+    ref_fma = _sha(oracle.gemm(a, b, fused=True))
+    assert runs[0]["gemm_fma0"] == ref_fma and runs[0]["gemm_fma1"] == ref_fma
+    st, g2 = C.adamw_hash_inputs()
+    hp = dict(C.AH_HP)
+    step = hp.pop("step")
+    oracle.adamw_inplace(st, g2, step=step, **hp)
+    assert runs[0]["adamw_hash_state"] == _sha(st)
+    assert runs[0]["adamw_hash_digest"] == oracle.state_hash(st).hex()
+    w, m, v, gb = C.bf16_inputs()
+    state = oracle.new_step_state()
+    for _ in range(3):
+        oracle.adamw_bf16_step(w, m, v, gb, state, **C.BF16_HP)
+    assert runs[0]["bf16_w"] == hashlib.sha256(w.tobytes()).hexdigest()
+    assert runs[0]["bf16_m"] == _sha(m)

@@ -108,10 +108,19 @@ def test_full_size_equals_the_two_calls():
     AC = synth.ADAMW
     n = AC["n"]
     print(f"adamw+hash n={n}", flush=True)
+    rng = np.random.default_rng(77)
+    idx = np.unique(rng.integers(0, n, 4000))
     st = torch.empty(3 * n, dtype=torch.float32, device="cuda")
+    parts = []
     for k, gen in enumerate((synth.adamw_w, synth.adamw_m, synth.adamw_v)):
-        st[k * n:(k + 1) * n].copy_(torch.from_numpy(gen()))
-    g = torch.from_numpy(synth.adamw_g()).cuda()
+        host = gen()
+        parts.append(host[idx].copy())
+        st[k * n:(k + 1) * n].copy_(torch.from_numpy(host))
+        del host
+    host = synth.adamw_g()
+    g_sample = host[idx].copy()
+    g = torch.from_numpy(host).cuda()
+    del host
     other = st.clone()
     third = st.clone()
     ws = br.hash_workspace(3 * n)
@@ -120,6 +129,20 @@ def test_full_size_equals_the_two_calls():
     d3 = torch.empty(32, dtype=torch.uint8, device="cuda")
     hp = dict(lr=AC["lr"], beta1=AC["beta1"], beta2=AC["beta2"], eps=AC["eps"], weight_decay=AC["wd"])
     br.repro_adamw_hash(st, g, d1, ws, step=AC["step"], **hp)
+    # Sampled leaves of the fused kernel's level 0 against the oracle, on the
+    # updated words, and sampled elements of the update itself.
+    nleaves = 3 * n // 1024
+    leaves = sorted({0, n // 1024 - 1, n // 1024, 2 * n // 1024, nleaves - 1} |
+                    set(rng.integers(0, nleaves, 11).tolist()))
+    lvl0 = ws[:32 * nleaves].view(nleaves, 32)
+    for leaf in leaves:
+        words = st[leaf * 1024:(leaf + 1) * 1024].cpu().numpy()
+        assert lvl0[leaf].cpu().numpy().tobytes() == oracle.state_hash_one_leaf(words, leaf, leaf == nleaves - 1), leaf
+    sample = np.concatenate(parts).astype(np.float32)
+    oracle.adamw_inplace(sample, g_sample, step=AC["step"], **hp)
+    tidx = torch.from_numpy(idx).cuda()
+    got = np.concatenate([st[:n][tidx].cpu().numpy(), st[n:2 * n][tidx].cpu().numpy(), st[2 * n:][tidx].cpu().numpy()])
+    assert_bitwise(got, sample, "full-size fused update, sampled")
     br.repro_adamw(other, g, step=AC["step"], **hp)
     br.repro_state_hash_async(other, d2, ws)
     assert torch.equal(st.view(torch.int32), other.view(torch.int32))
