@@ -288,7 +288,7 @@ def repro_state_hash(words, workspace=None, stream=None) -> bytes:
 
 def repro_adamw_hash(state, grad, digest_out, workspace, lr: float, beta1: float, beta2: float, eps: float,
                      weight_decay: float, step: int, chunk: int = 0, stream=None):
-    """repro_adamw then the state hash of the updated state, overlapped (see repro.h)."""
+    """repro_adamw then the state hash of the updated state, fused into one pass (see repro.h)."""
     n = grad.numel()
     if state.numel() != 3 * n or not state.is_contiguous() or not grad.is_contiguous():
         raise ValueError("state must hold 3n contiguous floats for a grad of n")
