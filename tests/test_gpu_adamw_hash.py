@@ -151,3 +151,33 @@ def test_full_size_equals_the_two_calls():
     br.repro_adamw_hash(third, g, d3, ws, step=AC["step"], chunk=1 << 26, **hp)
     assert torch.equal(st.view(torch.int32), third.view(torch.int32))
     assert torch.equal(d1, d3)
+
+
+def test_full_size_ten_repeats_and_the_oracle_digest():
+    # The bench step's fused call on the optimizer workload, ten times from
+    # the same state: ten identical digests, equal to the oracle's AdamW
+    # followed by its single-threaded BLAKE2b over all 14.4 GB.
+    AC = synth.ADAMW
+    n = AC["n"]
+    print(f"fused adamw+hash repeats n={n}", flush=True)
+    host = np.empty(3 * n, np.float32)
+    synth.adamw_w(n, out=host[:n])
+    synth.adamw_m(n, out=host[n:2 * n])
+    synth.adamw_v(n, out=host[2 * n:])
+    g = synth.adamw_g()
+    st0 = torch.from_numpy(host).cuda()
+    dg = torch.from_numpy(g).cuda()
+    ws = br.hash_workspace(3 * n)
+    hp = dict(lr=AC["lr"], beta1=AC["beta1"], beta2=AC["beta2"], eps=AC["eps"], weight_decay=AC["wd"])
+    digests = set()
+    for _ in range(10):
+        st = st0.clone()
+        d = torch.empty(32, dtype=torch.uint8, device="cuda")
+        br.repro_adamw_hash(st, dg, d, ws, step=AC["step"], **hp)
+        digests.add(bytes(d.cpu().numpy().tobytes()))
+        del st
+    assert len(digests) == 1
+    del st0
+    oracle.adamw_inplace(host, g, step=AC["step"], **hp)
+    print("oracle update done", flush=True)
+    assert digests.pop() == oracle.state_hash(host)
