@@ -278,28 +278,30 @@ __global__ __launch_bounds__(kTailNodes) void k_hash_tail(uint8_t* __restrict__ 
 // AdamW and the leaf level of the state hash in one pass (n a multiple of
 // 1024, so every 4 KiB leaf lies inside one of w, m and v).
 //
-// A workgroup of three waves owns kTriples leaf indices j and so the three
-// leaves w_j, m_j, v_j (leaf numbers j, n/1024 + j, 2n/1024 + j).  For each
-// of the 32 blocks b of a leaf, all 192 lanes first update elements
-// 1024 j + 32 b .. + 31 of every owned j (each wave instruction moves eight
-// whole 128-byte runs), store w', m', v' to HBM and the same bytes to LDS;
-// after a barrier wave r compresses block b of its region's leaves from
-// LDS, one lane per leaf.  A second barrier frees the LDS rows for block
-// b + 1.  The updated state is never read back from HBM.
-constexpr int kTriples = 64;
+// A workgroup is one wave; it owns kTriples = 21 leaf indices j and so the
+// 63 leaves w_j, m_j, v_j (leaf numbers j, n/1024 + j, 2n/1024 + j), one per
+// lane (lane 63 only helps with the update).  For each of the 32 blocks b of
+// a leaf, the wave updates elements 1024 j + 32 b .. + 31 of every owned j
+// (whole 128-byte runs of w, m, v, g), stores w', m', v' to HBM and the same
+// bytes to LDS, and then each lane compresses block b of its leaf from LDS.
+// The barriers between the two phases involve this wave alone, so waves
+// never wait for one another; the updated state is never read back.
+constexpr int kTriples = 21;
+constexpr int kFusedThreads = 64;
 
-__global__ __launch_bounds__(192) void k_adamw_hash_leaves(float* __restrict__ state, const float* __restrict__ grad,
-                                                           int64_t n, AdamwScalars s, uint8_t* __restrict__ out) {
+__global__ __launch_bounds__(kFusedThreads) void k_adamw_hash_leaves(float* __restrict__ state,
+                                                                     const float* __restrict__ grad, int64_t n,
+                                                                     AdamwScalars s, uint8_t* __restrict__ out) {
   // One 128-byte block per leaf, rows padded to 144 bytes so that 16 lanes
   // reading 16 bytes at a time from consecutive rows hit 64 distinct banks.
-  __shared__ uint4 rows[3][kTriples][9];
+  __shared__ uint4 rows[3 * kTriples][9];
   const int tid = threadIdx.x;
   const int64_t per_region = n / 1024;
   const int64_t j0 = (int64_t)blockIdx.x * kTriples;
   const int T = per_region - j0 < kTriples ? (int)(per_region - j0) : kTriples;
-  const int region = tid >> 6;
-  const int q = tid & 63;
-  const bool hashing = q < T;
+  const int region = tid / kTriples;
+  const int q = tid - region * kTriples;
+  const bool hashing = tid < 3 * kTriples && q < T;
   const int64_t leaf = region * per_region + j0 + q;
   const bool last_node = leaf == 3 * per_region - 1;
   uint64_t h[8];
@@ -309,7 +311,7 @@ __global__ __launch_bounds__(192) void k_adamw_hash_leaves(float* __restrict__ s
   float4* V = reinterpret_cast<float4*>(state + 2 * n);
   const float4* G = reinterpret_cast<const float4*>(grad);
   for (int b = 0; b < kLeafBytes / 128; ++b) {
-    for (int f = tid; f < 8 * T; f += 192) {
+    for (int f = tid; f < 8 * T; f += kFusedThreads) {
       const int qq = f >> 3;
       const int e4 = f & 7;
       const int64_t i4 = (j0 + qq) * 256 + 8 * b + e4;  // element (j0 + qq) * 1024 + 32 b + 4 e4
@@ -324,19 +326,19 @@ __global__ __launch_bounds__(192) void k_adamw_hash_leaves(float* __restrict__ s
       st_nt(w, W + i4);
       st_nt(m, M + i4);
       st_nt(v, V + i4);
-      rows[0][qq][e4] = make_uint4(__float_as_uint(w.x), __float_as_uint(w.y), __float_as_uint(w.z),
-                                   __float_as_uint(w.w));
-      rows[1][qq][e4] = make_uint4(__float_as_uint(m.x), __float_as_uint(m.y), __float_as_uint(m.z),
-                                   __float_as_uint(m.w));
-      rows[2][qq][e4] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
-                                   __float_as_uint(v.w));
+      rows[qq][e4] = make_uint4(__float_as_uint(w.x), __float_as_uint(w.y), __float_as_uint(w.z),
+                                __float_as_uint(w.w));
+      rows[kTriples + qq][e4] = make_uint4(__float_as_uint(m.x), __float_as_uint(m.y), __float_as_uint(m.z),
+                                           __float_as_uint(m.w));
+      rows[2 * kTriples + qq][e4] = make_uint4(__float_as_uint(v.x), __float_as_uint(v.y), __float_as_uint(v.z),
+                                               __float_as_uint(v.w));
     }
     __syncthreads();
     if (hashing) {
       uint64_t mw[16];
 #pragma unroll
       for (int k = 0; k < 8; ++k) {
-        const uint4 u = rows[region][q][k];
+        const uint4 u = rows[tid][k];
         mw[2 * k] = (uint64_t)u.x | ((uint64_t)u.y << 32);
         mw[2 * k + 1] = (uint64_t)u.z | ((uint64_t)u.w << 32);
       }
@@ -355,7 +357,7 @@ hipError_t launch_adamw_hash_fused(float* state, const float* grad, int64_t n, c
   if (n <= 0 || n % 1024 != 0) return hipErrorInvalidValue;
   const int64_t grid = (n / 1024 + kTriples - 1) / kTriples;
   if (grid > 0x7fffffff) return hipErrorInvalidValue;
-  hipLaunchKernelGGL(k_adamw_hash_leaves, dim3((unsigned)grid), dim3(192), 0, stream, state, grad, n, s,
+  hipLaunchKernelGGL(k_adamw_hash_leaves, dim3((unsigned)grid), dim3(kFusedThreads), 0, stream, state, grad, n, s,
                      ws + plan.offset[0]);
   const hipError_t e = hipGetLastError();
   if (e != hipSuccess) return e;
