@@ -81,8 +81,9 @@ __device__ __forceinline__ float4 load_terms(const void* src, int64_t e, int64_t
 
 // One workgroup (4 waves) folds terms [4096 b, 4096 b + 4096) of a length
 // len sequence as a perfect pairwise tree and writes out[b].  Wave w takes
-// [1024 w, 1024 w + 1024) as four chunks of 256; in a chunk lane l holds
-// terms 4l .. 4l+3.
+// [1024 w, 1024 w + 1024) as four chunks of 256 with lane l holding terms
+// 4l .. 4l+3 (binary32 terms), or as two chunks of 512 with lane l holding
+// 8l .. 8l+7 (bf16 terms); either way one wave instruction loads 1 KB.
 template <int SRC>
 __global__ __launch_bounds__(256) void k_norm_fold(const void* __restrict__ src, int64_t len, bool aligned,
                                                    float* __restrict__ out) {
@@ -91,19 +92,48 @@ __global__ __launch_bounds__(256) void k_norm_fold(const void* __restrict__ src,
   const int lane = threadIdx.x & 63;
   const int64_t base = b * kNormBlock + wave * 1024;
   const bool vec = aligned && (b + 1) * kNormBlock <= len;
-  float chunk[4];
+  float wsum;
+  if constexpr (SRC == 1) {
+    // bf16 terms: two chunks of 512, lane l holding terms 8l .. 8l+7 (one
+    // 16-byte load); the same perfect tree, levels 1-3 in the lane and 4-9
+    // across lanes, then the two chunks.
+    float chunk[2];
 #pragma unroll
-  for (int j = 0; j < 4; ++j) {
-    const float4 x = load_terms<SRC>(src, base + j * 256 + 4 * lane, len, vec);
-    float s = add_c(add_c(x.x, x.y), add_c(x.z, x.w));
-    // Levels 3..8: lane l and lane l ^ k hold neighbouring blocks; both
-    // form the same sum (IEEE addition commutes bit for bit).
+    for (int j = 0; j < 2; ++j) {
+      const int64_t e = base + j * 512 + 8 * lane;
+      float4 x, y;
+      if (vec) {
+        const uint4 h = *reinterpret_cast<const uint4*>(static_cast<const uint16_t*>(src) + e);
+        x = make_float4(widen_bf16(h.x), widen_bf16(h.x >> 16), widen_bf16(h.y), widen_bf16(h.y >> 16));
+        y = make_float4(widen_bf16(h.z), widen_bf16(h.z >> 16), widen_bf16(h.w), widen_bf16(h.w >> 16));
+        x = make_float4(mul_c(x.x, x.x), mul_c(x.y, x.y), mul_c(x.z, x.z), mul_c(x.w, x.w));
+        y = make_float4(mul_c(y.x, y.x), mul_c(y.y, y.y), mul_c(y.z, y.z), mul_c(y.w, y.w));
+      } else {
+        x = load_terms<1>(src, e, len, false);
+        y = load_terms<1>(src, e + 4, len, false);
+      }
+      float s = add_c(add_c(add_c(x.x, x.y), add_c(x.z, x.w)), add_c(add_c(y.x, y.y), add_c(y.z, y.w)));
 #pragma unroll
-    for (int k = 1; k < 64; k <<= 1) s = add_c(s, __shfl_xor(s, k, 64));
-    chunk[j] = s;
+      for (int k = 1; k < 64; k <<= 1) s = add_c(s, __shfl_xor(s, k, 64));
+      chunk[j] = s;
+    }
+    wsum = add_c(chunk[0], chunk[1]);
+  } else {
+    float chunk[4];
+#pragma unroll
+    for (int j = 0; j < 4; ++j) {
+      const float4 x = load_terms<SRC>(src, base + j * 256 + 4 * lane, len, vec);
+      float s = add_c(add_c(x.x, x.y), add_c(x.z, x.w));
+      // Levels 3..8: lane l and lane l ^ k hold neighbouring blocks; both
+      // form the same sum (IEEE addition commutes bit for bit).
+#pragma unroll
+      for (int k = 1; k < 64; k <<= 1) s = add_c(s, __shfl_xor(s, k, 64));
+      chunk[j] = s;
+    }
+    wsum = add_c(add_c(chunk[0], chunk[1]), add_c(chunk[2], chunk[3]));
   }
   __shared__ float wave_sum[4];
-  if (lane == 0) wave_sum[wave] = add_c(add_c(chunk[0], chunk[1]), add_c(chunk[2], chunk[3]));
+  if (lane == 0) wave_sum[wave] = wsum;
   __syncthreads();
   if (threadIdx.x == 0) out[b] = add_c(add_c(wave_sum[0], wave_sum[1]), add_c(wave_sum[2], wave_sum[3]));
 }
@@ -251,8 +281,8 @@ hipError_t launch_grad_norm(const void* g, int dtype, int64_t n, uint8_t* ws, co
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     float* out = plan.out_offset[p] < 0 ? &hdr->sumsq : reinterpret_cast<float*>(ws + plan.out_offset[p]);
     if (p == 0 && dtype == 1) {
-      hipLaunchKernelGGL(k_norm_fold<1>, dim3((unsigned)grid), dim3(256), 0, stream, src, len, aligned_to(src, 8),
-                         out);
+      hipLaunchKernelGGL(k_norm_fold<1>, dim3((unsigned)grid), dim3(256), 0, stream, src, len,
+                         aligned_to(src, 16), out);
     } else if (p == 0) {
       hipLaunchKernelGGL(k_norm_fold<0>, dim3((unsigned)grid), dim3(256), 0, stream, src, len,
                          aligned_to(src, 16), out);

@@ -55,6 +55,10 @@ def test_grad_norm_unaligned_order_witness_and_empty():
     ref = np.array(oracle.grad_norm(g[1:], return_sumsq=True), np.float32)
     out = to_host(br.repro_grad_norm(to_dev(g)[1:]))  # 4-byte aligned view: scalar loads
     assert_bitwise(out, ref, "unaligned view")
+    gb = _bf16_bits(g)
+    ref_b = np.array(oracle.grad_norm(gb[3:], return_sumsq=True), np.float32)
+    out_b = to_host(br.repro_grad_norm(_dev_bf16(gb)[3:]))  # 2-byte aligned bf16 view
+    assert_bitwise(out_b, ref_b, "unaligned bf16 view")
     w = np.ones(4096, np.float32)
     w[0] = 4096.0
     out = to_host(br.repro_grad_norm(to_dev(w)))
