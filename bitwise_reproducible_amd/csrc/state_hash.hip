@@ -15,7 +15,7 @@
 //    message schedule is resolved at compile time and the 16 message words,
 //    the 16 state words and the chaining value stay in VGPRs;
 //  - each block's eight 16-byte loads are issued right before it is
-//    compressed; at ~100 VGPRs five waves share a SIMD and hide the load
+//    compressed; at 100 VGPRs four waves share a SIMD and hide the load
 //    latency (prefetching the next block instead costs 32 more VGPRs, one
 //    wave fewer, and measured 2% slower);
 //  - upper levels with many nodes run one lane per node (a node reads 16
