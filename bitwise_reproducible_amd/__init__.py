@@ -106,10 +106,30 @@ def _stream(stream=None) -> int:
     return int(s.cuda_stream)
 
 
+def _on_device(t, name: str, dtype=None, min_bytes: int = 0):
+    """Check that t is a contiguous tensor on the current ROCm device (of dtype, holding at least
+    min_bytes): the library receives only its address, so a host or foreign-device tensor must
+    never reach it."""
+    import torch
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TypeError(f"{name} must be a tensor on a ROCm device")
+    if dtype is not None and t.dtype != dtype:
+        raise TypeError(f"{name} must be {dtype}, not {t.dtype}")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
+    if not t.is_contiguous():
+        raise ValueError(f"{name} must be contiguous")
+    if t.numel() * t.element_size() < min_bytes:
+        raise ValueError(f"{name} must hold at least {min_bytes} bytes")
+    return t
+
+
 def _f32_device(t, name: str):
     import torch
     if not isinstance(t, torch.Tensor) or t.dtype != torch.float32 or not t.is_cuda:
         raise TypeError(f"{name} must be a float32 tensor on a ROCm device")
+    if t.device.index != torch.cuda.current_device():
+        raise ValueError(f"{name} is on {t.device}, but the current device is cuda:{torch.cuda.current_device()}")
     return t
 
 
@@ -213,20 +233,35 @@ def repro_replay_reduce(grads, dp_replicate: int, dp_shard: int, accum: int, out
     return out
 
 
-def _slot_ptrs(slots):
-    ptrs = [s.data_ptr() if s is not None else None for s in slots]
+def _slot_ptrs(slots, n: int):
+    import torch
+    slots = list(slots)
+    if len(slots) > REPRO_FOLD_SLOTS:
+        raise ValueError(f"at most {REPRO_FOLD_SLOTS} slots")
+    for i, t in enumerate(slots):
+        if t is not None:
+            _on_device(t, f"slots[{i}]", torch.float32)
+            if t.numel() != n:
+                raise ValueError(f"slots[{i}] must hold {n} floats")
+    ptrs = [t.data_ptr() if t is not None else None for t in slots]
     ptrs += [None] * (REPRO_FOLD_SLOTS - len(ptrs))
     return (ctypes.c_void_p * REPRO_FOLD_SLOTS)(*ptrs)
 
 
 def repro_fold_push(slots, pushed: int, part, stream=None):
     """Push one partial into the caller-owned level slots (list of device tensors or None)."""
-    _check(library().repro_fold_push(ctypes.cast(_slot_ptrs(slots), ctypes.c_void_p), int(pushed), part.data_ptr(),
+    import torch
+    _on_device(part, "part", torch.float32)
+    ptrs = _slot_ptrs(slots, part.numel())
+    _check(library().repro_fold_push(ctypes.cast(ptrs, ctypes.c_void_p), int(pushed), part.data_ptr(),
                                      part.numel(), _stream(stream)), "repro_fold_push")
 
 
 def repro_fold_result(slots, pushed: int, out, divisor: int = 0, stream=None):
-    _check(library().repro_fold_result(ctypes.cast(_slot_ptrs(slots), ctypes.c_void_p), int(pushed), out.numel(),
+    import torch
+    _on_device(out, "out", torch.float32)
+    ptrs = _slot_ptrs(slots, out.numel())
+    _check(library().repro_fold_result(ctypes.cast(ptrs, ctypes.c_void_p), int(pushed), out.numel(),
                                        out.data_ptr(), int(divisor), _stream(stream)), "repro_fold_result")
     return out
 
@@ -265,11 +300,9 @@ def hash_workspace(n_words: int, device="cuda"):
 def repro_state_hash_async(words, digest_out, workspace, stream=None):
     """Enqueue the state hash; the 32-byte digest lands in ``digest_out`` (device uint8[32])."""
     import torch
-    _f32_device(words, "words")
-    if not words.is_contiguous():
-        raise ValueError("words must be contiguous")
-    if digest_out.dtype != torch.uint8 or digest_out.numel() < 32 or not digest_out.is_cuda:
-        raise ValueError("digest_out must be a device uint8 tensor of 32 bytes")
+    _on_device(words, "words", torch.float32)
+    _on_device(digest_out, "digest_out", torch.uint8, 32)
+    _on_device(workspace, "workspace", torch.uint8)
     st = library().repro_state_hash(words.data_ptr(), words.numel(), workspace.data_ptr(), workspace.numel(),
                                     digest_out.data_ptr(), _stream(stream))
     _check(st, "repro_state_hash")
@@ -289,9 +322,14 @@ def repro_state_hash(words, workspace=None, stream=None) -> bytes:
 def repro_adamw_hash(state, grad, digest_out, workspace, lr: float, beta1: float, beta2: float, eps: float,
                      weight_decay: float, step: int, chunk: int = 0, stream=None):
     """repro_adamw then the state hash of the updated state, fused into one pass (see repro.h)."""
+    import torch
+    _on_device(state, "state", torch.float32)
+    _on_device(grad, "grad", torch.float32)
+    _on_device(digest_out, "digest_out", torch.uint8, 32)
+    _on_device(workspace, "workspace", torch.uint8)
     n = grad.numel()
-    if state.numel() != 3 * n or not state.is_contiguous() or not grad.is_contiguous():
-        raise ValueError("state must hold 3n contiguous floats for a grad of n")
+    if state.numel() != 3 * n:
+        raise ValueError("state must hold 3n floats for a grad of n")
     _check(library().repro_adamw_hash(state.data_ptr(), grad.data_ptr(), n, lr, beta1, beta2, eps, weight_decay,
                                       int(step), workspace.data_ptr(), workspace.numel(), digest_out.data_ptr(),
                                       int(chunk), _stream(stream)), "repro_adamw_hash")
@@ -367,12 +405,13 @@ def read_step_state(state) -> dict:
 def repro_grad_norm(grad, workspace=None, out=None, stream=None):
     """Device tensor [norm, S]: the pre-clip global norm of a flat float32 or bfloat16 gradient."""
     import torch
-    if not grad.is_contiguous():
-        raise ValueError("grad must be contiguous")
+    _on_device(grad, "grad")
     if workspace is None:
         workspace = grad_norm_workspace(grad.numel(), grad.device)
     if out is None:
         out = torch.empty(2, dtype=torch.float32, device=grad.device)
+    _on_device(workspace, "workspace", torch.uint8)
+    _on_device(out, "out", torch.float32, 8)
     _check(library().repro_grad_norm(grad.data_ptr(), _grad_dtype(grad), grad.numel(), workspace.data_ptr(),
                                      workspace.numel(), out.data_ptr(), _stream(stream)), "repro_grad_norm")
     return out
@@ -387,10 +426,13 @@ def repro_adamw_bf16_step(w, m, v, grad, state, lr: float, beta1: float, beta2: 
         raise TypeError("w must be bfloat16, m and v float32")
     n = w.numel()
     for t, nm in ((w, "w"), (m, "m"), (v, "v"), (grad, "grad")):
-        if not t.is_contiguous() or t.numel() != n or not t.is_cuda:
-            raise ValueError(f"{nm} must be a contiguous device tensor of {n} elements")
+        _on_device(t, nm)
+        if t.numel() != n:
+            raise ValueError(f"{nm} must hold {n} elements")
+    _on_device(state, "state", torch.uint8, STEP_STATE_BYTES)
     if workspace is None:
         workspace = grad_norm_workspace(n, w.device)
+    _on_device(workspace, "workspace", torch.uint8)
     _check(library().repro_adamw_bf16_step(w.data_ptr(), m.data_ptr(), v.data_ptr(), grad.data_ptr(),
                                            _grad_dtype(grad), n, lr, beta1, beta2, eps, weight_decay, max_norm,
                                            spike_threshold, int(skip_steps), workspace.data_ptr(), workspace.numel(),

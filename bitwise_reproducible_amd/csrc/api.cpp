@@ -12,6 +12,14 @@
 #include "internal.h"
 #include "repro.h"
 
+// The host-side scalars below change the SSE control register around their
+// arithmetic; declaring access to the floating-point environment keeps the
+// compiler from moving that arithmetic across the change.  (This file has no
+// device code; the device pass does not know the pragma.)
+#ifndef __HIP_DEVICE_COMPILE__
+#pragma STDC FENV_ACCESS ON
+#endif
+
 namespace {
 
 using repro::AdamwScalars;
@@ -80,7 +88,7 @@ const char* repro_strerror(int status) {
   switch (status) {
     case REPRO_OK: return "ok";
     case REPRO_EINVAL: return "invalid argument";
-    case REPRO_EALIGN: return "device pointer not 4-byte aligned";
+    case REPRO_EALIGN: return "pointer not aligned as the call requires";
     case REPRO_EDEVICE: return "HIP launch or runtime error";
     case REPRO_ESPACE: return "workspace too small";
     default: return "unknown status";

@@ -32,8 +32,10 @@
  *     allocation, e.g. a torch tensor on a ROCm device) and must be aligned
  *     to 4 bytes.  16-byte alignment enables the vectorised kernels; other
  *     alignments take a slower path with identical results.
- *   - The caller owns every buffer.  The library allocates nothing and keeps
- *     no global state; calls are thread-safe.
+ *   - The caller owns every buffer.  The library allocates no device memory.
+ *     Its only global state is a pair of streams and a pool of events per
+ *     device, created by the first repro_adamw_hash call with chunk > 0 and
+ *     kept until the process ends.  Calls are thread-safe.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns without waiting.
  *   - Return value: REPRO_OK (0) or a negative REPRO_E* code.  On an error
@@ -51,7 +53,7 @@ extern "C" {
 
 #define REPRO_OK 0
 #define REPRO_EINVAL -1 /* null pointer, negative size, bad flag, R out of range, ld too small, step < 1 */
-#define REPRO_EALIGN -2 /* a device pointer is not 4-byte aligned */
+#define REPRO_EALIGN -2 /* a pointer is not aligned as the call requires (4 bytes unless stated) */
 #define REPRO_EDEVICE -3 /* HIP launch or runtime error */
 #define REPRO_ESPACE -4 /* workspace too small */
 
