@@ -21,7 +21,8 @@ def _grads(nbuf, n, tid0):
 
 
 @pytest.mark.parametrize("rep,shard,accum", [(1, 1, 1), (1, 3, 1), (2, 2, 2), (3, 5, 3), (8, 4, 2), (7, 1, 4),
-                                             (5, 8, 1), (64, 1, 1), (13, 2, 3)])
+                                             (5, 8, 1), (64, 1, 1), (13, 2, 3),
+                                             (64, 6, 1), (8, 8, 6)])  # the last two: REPRO_MAX_REPLAY_BUFFERS = 384
 def test_layouts(rep, shard, accum):
     n = 4099  # ragged tail after the 16-byte vectors
     grads = _grads(rep * shard * accum, n, 0xB000 + 97 * rep + 13 * shard + accum)
@@ -84,7 +85,7 @@ def test_push_into_the_free_slot():
     assert_bitwise(to_host(br.repro_fold_result(slots, R, out, divisor=R)), oracle.tree_reduce(parts), "in place")
 
 
-@pytest.mark.parametrize("R", [1, 2, 3, 5, 7, 8, 13, 16, 31])
+@pytest.mark.parametrize("R", [1, 2, 3, 5, 7, 8, 13, 16, 31, 64, 127])  # 127: all seven slots in use
 def test_streaming_fold(R):
     n = 10_001
     parts = _grads(R, n, 0xBA00 + R)
@@ -103,6 +104,8 @@ def test_errors():
     ptrs = (ctypes.c_void_p * 2)(d.data_ptr(), d.data_ptr())
     assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 65, 1, 1, 8, d.data_ptr(), None) == -1
     assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 1, 2, 0, 8, d.data_ptr(), None) == -1
+    many = (ctypes.c_void_p * 385)(*([d.data_ptr()] * 385))
+    assert lib.repro_replay_reduce(ctypes.cast(many, ctypes.c_void_p), 5, 7, 11, 8, d.data_ptr(), None) == -1  # 385
     assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 1, 2, 1, 8, d.data_ptr() + 2, None) == -2
     slots = (ctypes.c_void_p * 7)(d.data_ptr(), None, None, None, None, None, None)
     assert lib.repro_fold_push(ctypes.cast(slots, ctypes.c_void_p), 1, d.data_ptr(), 8, None) == -1  # needs slot 1
