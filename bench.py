@@ -129,9 +129,9 @@ class Upload:
 def main():
     args = parse()
     if args.gpus != 1:
-        print(f"bench.py measures one GPU: this build has no multi-GPU path (asked for --gpus {args.gpus}). "
-              "The operations shard by contiguous element ranges or output tiles with no change of bits; "
-              "the design is described in DESIGN.md.", file=sys.stderr)
+        print(f"bench.py measures one GPU; the library has no multi-GPU path (asked for --gpus {args.gpus}). "
+              "Reduce, AdamW and the hash would shard by contiguous element ranges and the GEMM by output "
+              "tiles, with no change of bits.", file=sys.stderr)
         sys.exit(2)
     import numpy as np
     import torch
@@ -400,7 +400,7 @@ def main():
     out = {
         "metric": METRIC, "value": round(value, 2), "unit": "GB/s", "n_gpus": 1, "steps": args.steps,
         "warmup": args.warmup, "ms_per_step": round(ms_per_step, 4), "higher_is_better": True, "scaling": "weak",
-        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded Philox4x64-10, recipes in DESIGN.md)",
+        "vs_baseline": None, "dtype": "f32", "data": "synthetic (seeded Philox4x64-10, one counter-based stream per tensor)",
         "config": {"workload": "reduce R=8 n=16777216; gemm 8192x2048 @ 2048x8192; adamw+state_hash n=1.2e9 "
                                "[w|m|v] 14.4 GB; dW 2048x8192 K=16384",
                    "parallelism": "none (1 GPU)"},
