@@ -351,7 +351,8 @@ def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
 
 
 def repro_fp32_fma(a, b, c, unit: int = 0, out=None, stream=None):
-    """out = fma(a, b, c) per element on one unit (0: v_fma_f32, 1: matrix core)."""
+    """out = fma(a, b, c) per element on one unit (0: v_fma_f32; 1, 2, 3: the matrix-core
+    instructions 32x32x1_2b, 16x16x1_4b, 4x4x1_16b)."""
     import torch
     for t, nm in ((a, "a"), (b, "b"), (c, "c")):
         _f32_device(t, nm)

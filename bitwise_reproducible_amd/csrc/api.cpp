@@ -414,7 +414,7 @@ int repro_adamw_bf16_step(uint16_t* w, float* m, float* v, const void* grad, int
 
 int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
                    void* stream) {
-  if (unit < 0 || unit > 1 || n < 0) return REPRO_EINVAL;
+  if (unit < 0 || unit > 3 || n < 0) return REPRO_EINVAL;
   if (n == 0) return REPRO_OK;
   if (a == nullptr || b == nullptr || c == nullptr || out == nullptr) return REPRO_EINVAL;
   if (!aligned4(a) || !aligned4(b) || !aligned4(c) || !aligned4(out)) return REPRO_EALIGN;

@@ -370,11 +370,13 @@ int repro_fp32_ops(int32_t op, const float* a, const float* b, float* out, int64
 
 /*
  * repro_fp32_fma: out[i] = fma(a[i], b[i], c[i]) under the fused convention
- * of repro_gemm_fma, on one chosen unit: 0 = VALU v_fma_f32, 1 = the matrix
- * core instruction v_mfma_f32_32x32x1_2b_f32 (each element placed on the
- * diagonal of a 32x32 block, with c[i] as the C operand).  For directed
- * tests of the single step each fused GEMM variant repeats.  Device pointers
- * of n floats; out may be the same pointer as a, b or c (no partial overlap).
+ * of repro_gemm_fma, on one chosen unit: 0 = VALU v_fma_f32; 1, 2, 3 = the
+ * matrix-core instructions with K = 1, v_mfma_f32_32x32x1_2b_f32,
+ * v_mfma_f32_16x16x1_4b_f32 and v_mfma_f32_4x4x1_16b_f32 (each element
+ * placed on the diagonal of a block, with c[i] as the C operand).  For
+ * directed tests of the single step a fused chain repeats on each unit.
+ * Device pointers of n floats; out may be the same pointer as a, b or c (no
+ * partial overlap).
  */
 int repro_fp32_fma(const float* a, const float* b, const float* c, float* out, int64_t n, int32_t unit,
                    void* stream);

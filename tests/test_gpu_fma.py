@@ -7,6 +7,8 @@ subnormal rule.  Before any GEMM is trusted, each unit's single step is
 compared with the oracle's fma on directed operand sets:
   unit 0 - VALU v_fma_f32
   unit 1 - v_mfma_f32_32x32x1_2b_f32 with the chain value as C (K = 1)
+  unit 2 - v_mfma_f32_16x16x1_4b_f32, the same way
+  unit 3 - v_mfma_f32_4x4x1_16b_f32, the same way
 """
 import numpy as np
 import pytest
@@ -19,7 +21,7 @@ from parity_util import assert_bitwise, to_dev, to_host
 
 pytestmark = pytest.mark.gpu
 
-UNITS = [0, 1]
+UNITS = [0, 1, 2, 3]
 
 
 def _triples(seed, n):
@@ -68,12 +70,13 @@ def test_single_step_matches_oracle(unit):
         assert_bitwise(got, ref, f"unit {unit} set {si}")
 
 
+@pytest.mark.parametrize("unit", [1, 2, 3])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 130, 4097])
-def test_mfma_unit_ragged_groups(n):
+def test_mfma_unit_ragged_groups(n, unit):
     a, b, c = (synth.generate(n, synth.NORMAL, 0x9100 + i, 1.0) for i in range(3))
     out = torch.full((n + 64,), 7.0, device="cuda")
-    br.repro_fp32_fma(to_dev(a), to_dev(b), to_dev(c), unit=1, out=out[:n])
-    assert_bitwise(to_host(out[:n]), oracle.fma(a, b, c), f"n={n}")
+    br.repro_fp32_fma(to_dev(a), to_dev(b), to_dev(c), unit=unit, out=out[:n])
+    assert_bitwise(to_host(out[:n]), oracle.fma(a, b, c), f"n={n} unit={unit}")
     assert (to_host(out[n:]) == 7.0).all()  # nothing past the end was written
 
 
@@ -177,6 +180,6 @@ def test_errors():
     p = d.data_ptr()
     assert lib.repro_gemm_fma(0, 0, 2, 2, 2, p, 2, p, 2, p, 2, 2, None) == -1  # no variant 2
     assert lib.repro_gemm_fma(0, 0, 2, 2, 2, p + 2, 2, p, 2, p, 2, 0, None) == -2
-    assert lib.repro_fp32_fma(p, p, p, p, 4, 2, None) == -1
+    assert lib.repro_fp32_fma(p, p, p, p, 4, 4, None) == -1  # units 0..3
     assert lib.repro_fp32_fma(p, p, p + 1, p, 4, 0, None) == -2
     assert lib.repro_fp32_fma(p, p, p, p, 0, 1, None) == 0

@@ -88,7 +88,11 @@ def test_fused_kernels_use_the_declared_units(kernels):
             assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 1024
             assert ops["v_add_f32_e32"] == 0
         elif s == "k_fma_mfma":
-            assert ops["v_mfma_f32_32x32x1_2b_f32"] == 1
+            # One K = 1 matrix instruction per instantiation (32x32, 16x16 or 4x4 blocks).
+            shapes = [op for op in ("v_mfma_f32_32x32x1_2b_f32", "v_mfma_f32_16x16x1_4b_f32",
+                                    "v_mfma_f32_4x4x1_16b_f32") if ops[op]]
+            assert len(shapes) == 1 and ops[shapes[0]] == 1, ops
+            assert not any(FUSED_OR_PACKED.match(op) for op in ops)
         elif s == "k_fma_valu":
             assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 1
         else:
