@@ -329,6 +329,23 @@ def main():
         br.repro_tree_reduce([reps[0]], out=g_red, average=False)
         torch.cuda.synchronize()
 
+    # A plain copy for the secondary fractions: the one-replica fold without
+    # the average reads and writes each word once (2 GiB in, 2 GiB out).
+    copy_n = 1 << 29
+    c_src = torch.ones(copy_n, dtype=torch.float32, device=dev)
+    c_dst = torch.empty_like(c_src)
+    c_ms = []
+    for i in range(3 + 10):
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        br.repro_tree_reduce([c_src], out=c_dst, average=False)
+        e1.record()
+        c_ms.append((e0, e1))
+    torch.cuda.synchronize()
+    copy_ms = float(np.median([e0.elapsed_time(e1) for e0, e1 in c_ms[3:]]))
+    copy_gbps = 8 * copy_n / (copy_ms * 1e-3) / 1e9
+    del c_src, c_dst
+
     # Algorithmic work per launch.
     bytes_reduce = (RC["R"] + 1) * 4 * RC["n"]
     bytes_adamw = 28 * n
@@ -357,7 +374,8 @@ def main():
             return {"bound": "alu" if t_alu >= t_hbm else "hbm", "achieved": round(ach, 1), "peak": round(peak, 1),
                     "unit": "GB/s (of state hashed)", "frac": round(ach / peak, 4), "traffic": None,
                     "hbm_achieved": round(bytes_adamw / (ms * 1e-3) / 1e9, 1),
-                    "frac_of_hbm_peak": round(bytes_adamw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4)}
+                    "frac_of_hbm_peak": round(bytes_adamw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+                    "hbm_frac_of_copy": round(bytes_adamw / (ms * 1e-3) / 1e9 / copy_gbps, 4)}
         b = {"tree_reduce": bytes_reduce, "adamw": bytes_adamw, "state_hash": bytes_hash}[op]
         ach = b / (ms * 1e-3) / 1e9
         if op == "state_hash":  # integer-VALU bound: ~24 issue slots per byte
@@ -365,7 +383,7 @@ def main():
                     "frac": round(ach / HASH_PEAK_GBS, 4), "traffic": None,
                     "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4)}
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None}
+                "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "frac_of_copy": round(ach / copy_gbps, 4)}
 
     per_op = {op: {"ms": round(op_ms[op], 4), "ms_median": round(float(np.median(op_samples[op])), 4),
                    "ms_min": round(float(np.min(op_samples[op])), 4), **roof(op, op_ms[op])} for op in ops}
@@ -382,13 +400,15 @@ def main():
         "workload": f"dp_replicate={p_layout[0]} dp_shard={p_layout[1]} accum={p_layout[2]} "
                     f"({p_nbuf} buffers) n={PC['n']}",
         "ms": round(replay_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce")}}
+        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("replay_reduce"),
+        "frac_of_copy": round(ach / copy_gbps, 4)}}
     bytes_bf16 = 24 * n  # norm pass reads g (2n); update reads w, m, v, g (12n), writes w, m, v (10n)
     ach = bytes_bf16 / (bf16_ms * 1e-3) / 1e9
     next_rows["adamw_bf16_step"] = {
         "workload": f"n={n} bf16 w, fp32 m and v, bf16 g (norm ~3.5, clipped to 1.0), beta2 0.95",
         "ms": round(bf16_ms, 4), "bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
-        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("adamw_bf16_step")}
+        "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": traffic.get("adamw_bf16_step"),
+        "frac_of_copy": round(ach / copy_gbps, 4)}
     for variant, unit in ((0, "matrix cores, v_mfma_f32_32x32x1_2b_f32"), (1, "VALU, v_fma_f32")):
         ms = fma_ms[(variant, "fwd")] + fma_ms[(variant, "dw")]
         ach = (flops_fwd + flops_dw) / (ms * 1e-3) / 1e12
@@ -405,6 +425,8 @@ def main():
                                "[w|m|v] 14.4 GB; dW 2048x8192 K=16384",
                    "parallelism": "none (1 GPU)"},
         "gemm": {"value": round(gemm_gflops, 1), "unit": "GFLOP/s"},
+        "hbm_copy": {"gbps": round(copy_gbps, 1), "ms_median": round(copy_ms, 4), "bytes": 8 * copy_n,
+                     "kernel": "k_tree_reduce_v4<1, false> (one-replica fold: a plain copy)"},
         "ops": per_op,
         "ops_in_turn": in_turn,
         "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if not k.startswith("ms")}},
@@ -586,6 +608,13 @@ def cpu_baseline(np):
     g = synth.adamw_g(n_adam)
     x = synth.gemm_x(rows=16).reshape(16, 2048)
     bt = np.ascontiguousarray(synth.gemm_w().reshape(2048, 8192).T)
+    # One thread on one core: the calling thread is pinned for the timed part.
+    try:
+        saved = os.sched_getaffinity(0)
+        core = min(saved)
+        os.sched_setaffinity(0, {core})
+    except (AttributeError, OSError):
+        saved, core = None, None
     t0 = time.perf_counter()
     oracle.tree_reduce(reps)
     t1 = time.perf_counter()
@@ -595,12 +624,14 @@ def cpu_baseline(np):
     t3 = time.perf_counter()
     oracle.gemm(x, bt, trans_b=True)
     t4 = time.perf_counter()
+    if saved is not None:
+        os.sched_setaffinity(0, saved)
     nbytes = 9 * 4 * n_red + 28 * n_adam + 12 * n_adam
     return {"value": round(nbytes / (t3 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "gemm_gflops": round(2 * 16 * 8192 * 2048 / (t4 - t3) / 1e9, 4),
             "sample": f"the reduce workload (R=8 n={n_red}) and 2/3 of the optimizer workload (adamw + state_hash "
                       f"n={n_adam}); gemm: 16 rows of 8192x2048x8192; single-threaded oracle, {t4 - t0:.1f} s",
-            "host_cpu": _cpu_model(), "host_threads": os.cpu_count()}
+            "host_cpu": _cpu_model(), "host_threads": os.cpu_count(), "pinned_core": core}
 
 
 def _cpu_model():
