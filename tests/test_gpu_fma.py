@@ -100,6 +100,19 @@ def test_fused_gemm_shapes_transposes_variants(M, N, K, ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant={variant}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fused_several_tiles_with_ragged_edges(ta, tb):
+    M, N, K = 300, 400, 500  # 3 x 4 tiles, partial last tiles and a partial last k-slab of 32
+    tid = 0x9800 + 2 * ta + tb
+    A = _mat(K, M, tid) if ta else _mat(M, K, tid)
+    B = _mat(N, K, tid + 1, 0.5) if tb else _mat(K, N, tid + 1, 0.5)
+    ref = oracle.gemm(A, B, bool(ta), bool(tb), fused=True)
+    dA, dB = to_dev(A), to_dev(B)
+    for variant in (0, 1):
+        C = br.repro_gemm_fma(dA, dB, bool(ta), bool(tb), variant=variant)
+        assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant={variant}")
+
+
 def test_fused_witness_and_difference_from_unfused():
     t = np.float32(1.0 + 2.0 ** -12)
     A = np.array([[-1.0, t]], np.float32)

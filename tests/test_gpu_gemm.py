@@ -42,6 +42,19 @@ def test_shapes_transposes_variants(M, N, K, ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
 
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_many_tiles_with_ragged_edges(ta, tb):
+    # 1000 x 1500 x 700: 8 x 12 tiles of 128 with partial last tiles in M and
+    # N, and 43 full k-slabs of 16 plus a partial one, for every variant.
+    M, N, K = 1000, 1500, 700
+    A, B = _stored(M, N, K, ta, tb, 0x8800 + 2 * ta + tb)
+    ref = oracle.gemm(A, B, bool(ta), bool(tb))
+    dA, dB = to_dev(A), to_dev(B)
+    for variant in (0, 1, 2, 3):
+        C = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=variant)
+        assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
+
+
 def test_tiny_workload():
     a, b = synth.tiny_gemm_inputs()
     C = br.repro_gemm(to_dev(a), to_dev(b))
