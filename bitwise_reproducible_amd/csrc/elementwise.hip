@@ -79,7 +79,7 @@ static_assert(REPRO_MAX_REPLICAS <= 127, "fold_rest walks bits 0..6");
 // vectors; measured on MI355X this shape streams faster than a grid-stride
 // loop).  AVG selects the multiply by fl(1/R) at compile time.
 template <int R, bool AVG>
-__global__ __launch_bounds__(256) void k_tree_reduce_v4(ReplicaPtrs reps, float4* __restrict__ out, int64_t n4,
+__global__ __launch_bounds__(kStreamLanes) void k_tree_reduce_v4(ReplicaPtrs reps, float4* __restrict__ out, int64_t n4,
                                                          float rR) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
   if (i >= n4) return;
@@ -153,7 +153,7 @@ bool aligned16(const void* p) { return (reinterpret_cast<uintptr_t>(p) & 15u) ==
 
 // ---------------------------------------------------------------------------
 // AdamW (section 3.2 "Optimizer"): adamw_elem in device_ops.h.
-__global__ __launch_bounds__(256) void k_adamw_v4(float4* __restrict__ w4, float4* __restrict__ m4,
+__global__ __launch_bounds__(kStreamLanes) void k_adamw_v4(float4* __restrict__ w4, float4* __restrict__ m4,
                                                    float4* __restrict__ v4, const float4* __restrict__ g4,
                                                    int64_t n4, AdamwScalars s) {
   const int64_t i = (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -216,9 +216,10 @@ hipError_t launch_tree_reduce(const ReplicaPtrs& reps, int R, int64_t n, float* 
       hipLaunchKernelGGL(kV4StridedTable[R - 1], dim3((unsigned)grid_for(n4, 64, 1024)), dim3(64), 0, stream, reps,
                          reinterpret_cast<float4*>(out), n4, rR, average);
     } else {
-      const int64_t grid = (n4 + 255) / 256;
+      const int64_t grid = (n4 + kStreamLanes - 1) / kStreamLanes;
       if (grid > 0x7fffffff) return hipErrorInvalidValue;
-      hipLaunchKernelGGL((average ? kV4AvgTable : kV4Table)[R - 1], dim3((unsigned)grid), dim3(256), 0, stream,
+      hipLaunchKernelGGL((average ? kV4AvgTable : kV4Table)[R - 1], dim3((unsigned)grid), dim3(kStreamLanes), 0,
+                         stream,
                          reps, reinterpret_cast<float4*>(out), n4, rR);
     }
   }
@@ -241,9 +242,9 @@ hipError_t launch_adamw_ptrs(float* w, float* m, float* v, const float* grad, in
   const bool vec = variant != 1 && aligned16(w) && aligned16(m) && aligned16(v) && aligned16(grad);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {
-    const int64_t grid = (n4 + 255) / 256;
+    const int64_t grid = (n4 + kStreamLanes - 1) / kStreamLanes;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_adamw_v4, dim3((unsigned)grid), dim3(256), 0, stream, reinterpret_cast<float4*>(w),
+    hipLaunchKernelGGL(k_adamw_v4, dim3((unsigned)grid), dim3(kStreamLanes), 0, stream, reinterpret_cast<float4*>(w),
                        reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v),
                        reinterpret_cast<const float4*>(grad), n4, s);
   }

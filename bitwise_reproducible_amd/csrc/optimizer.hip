@@ -204,7 +204,7 @@ __device__ __forceinline__ float clip_grad(float g, float coef) { return coef < 
 // Four elements per thread over an exact grid of n/4 threads.  GBF16: the
 // gradient is bf16 (else binary32).
 template <bool GBF16>
-__global__ __launch_bounds__(256) void k_adamw_bf16_v4(uint2* __restrict__ w4, float4* __restrict__ m4,
+__global__ __launch_bounds__(kStreamLanes) void k_adamw_bf16_v4(uint2* __restrict__ w4, float4* __restrict__ m4,
                                                        float4* __restrict__ v4, const void* __restrict__ g,
                                                        int64_t n4, const OptHeader* __restrict__ hdr, float lr,
                                                        float beta1, float beta2, float eps, float wd) {
@@ -302,14 +302,14 @@ hipError_t launch_adamw_bf16(uint16_t* w, float* m, float* v, const void* g, int
   const bool vec = aligned_to(w, 8) && aligned_to(m, 16) && aligned_to(v, 16) && aligned_to(g, dtype == 1 ? 8 : 16);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {
-    const int64_t grid = (n4 + 255) / 256;
+    const int64_t grid = (n4 + kStreamLanes - 1) / kStreamLanes;
     if (grid > 0x7fffffff) return hipErrorInvalidValue;
     if (dtype == 1)
-      hipLaunchKernelGGL(k_adamw_bf16_v4<true>, dim3((unsigned)grid), dim3(256), 0, stream,
+      hipLaunchKernelGGL(k_adamw_bf16_v4<true>, dim3((unsigned)grid), dim3(kStreamLanes), 0, stream,
                          reinterpret_cast<uint2*>(w), reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v), g,
                          n4, hdr, lr, beta1, beta2, eps, wd);
     else
-      hipLaunchKernelGGL(k_adamw_bf16_v4<false>, dim3((unsigned)grid), dim3(256), 0, stream,
+      hipLaunchKernelGGL(k_adamw_bf16_v4<false>, dim3((unsigned)grid), dim3(kStreamLanes), 0, stream,
                          reinterpret_cast<uint2*>(w), reinterpret_cast<float4*>(m), reinterpret_cast<float4*>(v), g,
                          n4, hdr, lr, beta1, beta2, eps, wd);
   }

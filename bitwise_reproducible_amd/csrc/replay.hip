@@ -73,7 +73,7 @@ __device__ __forceinline__ void push_regs(Elem<VEC> (&st)[kLevels], int pushed, 
 
 // Elements [first, count) (16-byte vectors when VEC).
 template <bool VEC>
-__global__ __launch_bounds__(256) void k_replay(ReplayPtrs a, int dp_replicate, int dp_shard, int accum,
+__global__ __launch_bounds__(kStreamLanes) void k_replay(ReplayPtrs a, int dp_replicate, int dp_shard, int accum,
                                                 float r_accum, float r_shard, float r_rep, float* out,
                                                 int64_t first, int64_t count) {
   const int64_t i = first + (int64_t)blockIdx.x * blockDim.x + threadIdx.x;
@@ -140,14 +140,16 @@ hipError_t launch_replay(const ReplayPtrs& a, int nbuf, int dp_replicate, int dp
   for (int b = 0; b < nbuf; ++b) vec = vec && al16(a.p[b]);
   const int64_t n4 = vec ? n / 4 : 0;
   if (n4 > 0) {
-    if ((n4 + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_replay<true>, dim3(grid_of(n4)), dim3(256), 0, stream, a, dp_replicate, dp_shard, accum,
+    if ((n4 + kStreamLanes - 1) / kStreamLanes > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_replay<true>, dim3((unsigned)((n4 + kStreamLanes - 1) / kStreamLanes)), dim3(kStreamLanes), 0,
+                       stream, a, dp_replicate, dp_shard, accum,
                        r_accum, r_shard, r_rep, out, int64_t(0), n4);
   }
   if (4 * n4 < n) {
     const int64_t first = 4 * n4;
-    if ((n - first + 255) / 256 > 0x7fffffff) return hipErrorInvalidValue;
-    hipLaunchKernelGGL(k_replay<false>, dim3(grid_of(n - first)), dim3(256), 0, stream, a, dp_replicate, dp_shard,
+    if ((n - first + kStreamLanes - 1) / kStreamLanes > 0x7fffffff) return hipErrorInvalidValue;
+    hipLaunchKernelGGL(k_replay<false>, dim3((unsigned)((n - first + kStreamLanes - 1) / kStreamLanes)),
+                       dim3(kStreamLanes), 0, stream, a, dp_replicate, dp_shard,
                        accum, r_accum, r_shard, r_rep, out, first, n);
   }
   return hipGetLastError();

@@ -145,7 +145,7 @@ int repro_gemm_fma(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, co
 int repro_tree_reduce(const float* const* replicas, int32_t R, int64_t n, float* out, int32_t average,
                       void* stream);
 
-/* Variant 0 default (16-byte vectors, 256 threads); 1 scalar elements;
+/* Variant 0 default (16-byte vectors, one-wave workgroups); 1 scalar elements;
  * 2 16-byte vectors, 64 threads and a grid-stride loop over a small grid. */
 int repro_tree_reduce_variant(const float* const* replicas, int32_t R, int64_t n, float* out,
                               int32_t average, int32_t variant, void* stream);
