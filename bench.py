@@ -254,6 +254,16 @@ def main():
     ms_per_step = (t1 - t0) * 1e3 / args.steps
     op_samples = {op: [evs[s][i].elapsed_time(evs[s][i + 1]) for s in range(args.steps)] for i, op in enumerate(ops)}
     op_ms = {op: float(np.mean(v)) for op, v in op_samples.items()}
+    # Digests of every op's output after the last step (untimed; state hash
+    # of the words).  With the same --steps and --warmup they are the same on
+    # every run, box and process.
+    dg_ws = br.hash_workspace(RC["n"] if RC["n"] > GC["M"] * GC["N"] else GC["M"] * GC["N"], dev)
+    digests = {"steps_taken": args.warmup + args.steps,
+               "tree_reduce_out": br.repro_state_hash(g_red, dg_ws).hex(),
+               "gemm_fwd_out": br.repro_state_hash(Y3.view(-1), dg_ws).hex(),
+               "gemm_dw_out": br.repro_state_hash(dW5.view(-1), dg_ws).hex(),
+               "adamw_state": bytes(digest.cpu().numpy().tobytes()).hex()}
+    del dg_ws
 
     # The replay, timed on its own: same warmup and count as the steps.
     for _ in range(args.warmup):
@@ -431,6 +441,7 @@ def main():
         "ops_in_turn": in_turn,
         "roofline": {"kernel": dominant, **{k: v for k, v in per_op[dominant].items() if not k.startswith("ms")}},
         "next_rows": next_rows,
+        "digests": digests,
     }
 
     if not args.no_verify:
