@@ -134,15 +134,22 @@ def _f32_device(t, name: str):
 
 
 def _row_major(t, name: str):
-    """(pointer, rows, cols, ld) of a 2-D float32 device tensor with unit column stride."""
+    """(pointer, rows, cols, ld) of a 2-D float32 device tensor with unit column stride.
+
+    The library reads row i at pointer + i * ld, so rows must not overlap: a view
+    whose row stride is below its width (an expand() or an overlapping as_strided)
+    is refused rather than passed with a larger ld that would address memory
+    outside the tensor's storage."""
     _f32_device(t, name)
     if t.dim() != 2:
         raise ValueError(f"{name} must be 2-D")
     rows, cols = t.shape
     if cols > 1 and t.stride(1) != 1:
         raise ValueError(f"{name} needs unit stride along its last dimension")
+    if rows > 1 and t.stride(0) < cols:
+        raise ValueError(f"{name} has row stride {t.stride(0)} below its {cols} columns (overlapping rows)")
     ld = t.stride(0) if rows > 1 else max(cols, 1)
-    return t.data_ptr(), rows, cols, max(ld, cols, 1)
+    return t.data_ptr(), rows, cols, max(ld, 1)
 
 
 def repro_gemm(A, B, trans_a: bool = False, trans_b: bool = False, out=None, variant: int = 0, stream=None,

@@ -158,6 +158,8 @@ int repro_replay_reduce(const float* const* grads, int32_t dp_replicate, int32_t
   if (grads == nullptr || dp_replicate < 1 || dp_replicate > REPRO_MAX_REPLICAS || dp_shard < 1 || accum < 1 ||
       n < 0)
     return REPRO_EINVAL;
+  // Each factor is bounded before the product is formed, so it cannot wrap.
+  if (dp_shard > REPRO_MAX_REPLAY_BUFFERS || accum > REPRO_MAX_REPLAY_BUFFERS) return REPRO_EINVAL;
   const int64_t nbuf = (int64_t)dp_replicate * dp_shard * accum;
   if (nbuf > REPRO_MAX_REPLAY_BUFFERS) return REPRO_EINVAL;
   if (n == 0) return REPRO_OK;

@@ -48,3 +48,26 @@ def test_every_compute_wrapper_is_covered():
     compute = {n for n in br.__all__ if n.startswith("repro_") and n != "repro_state_hash_workspace_bytes"}
     compute.discard("repro_state_hash")  # allocates its digest on the words' device, then calls the async form
     assert compute <= set(CASES), sorted(compute - set(CASES))
+
+
+def test_overlapping_rows_are_refused(monkeypatch):
+    # The GEMM reads row i at base + i * ld.  A view whose row stride is below
+    # its width (expand, an overlapping as_strided) would make the library read
+    # or write past the storage, so the binding refuses it before any call.  The
+    # device check is bypassed so that host tensors can stand in (no call is made).
+    monkeypatch.setattr(br, "_f32_device", lambda t, name: t)
+    expanded = torch.zeros(1, 64).expand(64, 64)
+    with pytest.raises(ValueError, match="overlapping rows"):
+        br._row_major(expanded, "A")
+    overlap = torch.zeros(200).as_strided((8, 64), (16, 1))
+    with pytest.raises(ValueError, match="overlapping rows"):
+        br._row_major(overlap, "out")
+    with pytest.raises(ValueError, match="overlapping rows"):
+        br.repro_gemm(torch.zeros(64, 64), expanded)
+    with pytest.raises(ValueError, match="overlapping rows"):
+        br.repro_gemm(torch.zeros(64, 64), torch.zeros(64, 64), out=torch.zeros(64).expand(64, 64))
+    # Accepted views keep their own row stride as ld.
+    base = torch.zeros(10, 80)
+    assert br._row_major(base[:, 8:72], "A")[1:] == (10, 64, 80)
+    assert br._row_major(torch.zeros(1, 5), "A")[1:] == (1, 5, 5)
+    assert br._row_major(torch.zeros(7, 1)[:, :1], "A")[1:] == (7, 1, 1)

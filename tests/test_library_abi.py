@@ -52,6 +52,12 @@ def test_host_side_argument_checks():
     assert lib.repro_fp32_ops(7, 16, 16, 16, 4, null) == -1
     assert lib.repro_state_hash(16, -1, 16, 1 << 20, 16, null) == -1
     assert lib.repro_state_hash(16, 1024, 16, 0, 16, null) == -4  # workspace too small
+    # Replay: buffer counts whose product would wrap int64 (64 * 2^31-1 * 2^31-1)
+    # or exceed the buffer limit are refused before the pointer array is read.
+    big = 2**31 - 1
+    assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 64, big, big, 4, 16, null) == -1
+    assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 1, 1 << 30, 1 << 28, 4, 16, null) == -1
+    assert lib.repro_replay_reduce(ctypes.cast(ptrs, ctypes.c_void_p), 2, 1, 193, 4, 16, null) == -1
 
 
 def _plan_bytes(n_words):
