@@ -1,10 +1,18 @@
 """Child process for the cross-process determinism test.
 
-Runs the tiny chained workload (GEMM, TreeFold, AdamW, state hash), the full
-gradient-reduction workload, and small cases of the audit replay, the fused
-GEMM convention (both units), the fused AdamW + hash and the BF16 optimizer
-step, ten times each in a fresh process, and prints one JSON line of SHA-256
-digests of the output words.
+Default mode: runs the tiny chained workload (GEMM, TreeFold, AdamW, state
+hash), the full gradient-reduction workload, and small cases of the audit
+replay, the fused GEMM convention (both units), the fused AdamW + hash and the
+BF16 optimizer step, ten times each in a fresh process, and prints one JSON
+line of SHA-256 digests of the output words.
+
+``--full``: the four full-size workloads, ten runs each in this process, every
+output reduced on the GPU to its 32-byte state hash (repro_state_hash):
+TreeFold over 8 x 16,777,216; the forward GEMM 8192 x 2048 x 8192; the weight
+gradient X^T dY with K = 16,384; the fused AdamW + state hash on the
+1.2e9-parameter [w | m | v] from the same initial state each run (the fused
+call's own digest and a separate state hash of the updated state).  Prints one
+JSON line of hex digests per run.
 """
 import hashlib
 import json
@@ -100,5 +108,70 @@ def main():
     print(json.dumps(out), flush=True)
 
 
+def _digest(t, ws) -> str:
+    return br.repro_state_hash(t.reshape(-1), ws).hex()
+
+
+def main_full():
+    dev = torch.device("cuda:0")
+    out = {"pid": os.getpid()}
+    runs = [dict() for _ in range(10)]
+
+    def stage(name):
+        print(f"full-size stage: {name}", file=sys.stderr, flush=True)
+
+    stage("tree reduce")
+    reps = [torch.from_numpy(synth.reduce_replica(r)).to(dev) for r in range(synth.REDUCE["R"])]
+    ws = br.hash_workspace(synth.REDUCE["n"], dev)
+    for r in runs:
+        r["reduce"] = _digest(br.repro_tree_reduce(reps), ws)
+    del reps, ws
+    stage("forward gemm")
+    cfg = synth.GEMM
+    X = torch.from_numpy(synth.gemm_x()).to(dev).view(cfg["M"], cfg["K"])
+    W = torch.from_numpy(synth.gemm_w()).to(dev).view(cfg["K"], cfg["N"])
+    Y = torch.empty(cfg["M"], cfg["N"], dtype=torch.float32, device=dev)
+    ws = br.hash_workspace(Y.numel(), dev)
+    for r in runs:
+        Y.fill_(7.0)
+        br.repro_gemm(X, W, out=Y)
+        r["gemm_fwd"] = _digest(Y, ws)
+    del X, W, Y, ws
+    stage("weight gradient gemm")
+    cfg = synth.DW
+    Xd = torch.from_numpy(synth.dw_x()).to(dev).view(cfg["K"], cfg["M"])
+    dY = torch.from_numpy(synth.dw_dy()).to(dev).view(cfg["K"], cfg["N"])
+    dW = torch.empty(cfg["M"], cfg["N"], dtype=torch.float32, device=dev)
+    ws = br.hash_workspace(dW.numel(), dev)
+    for r in runs:
+        dW.fill_(7.0)
+        br.repro_gemm(Xd, dY, trans_a=True, out=dW)
+        r["gemm_dw"] = _digest(dW, ws)
+    del Xd, dY, dW, ws
+    stage("fused adamw + state hash, n = 1.2e9")
+    cfg = synth.ADAMW
+    n = cfg["n"]
+    host = np.empty(3 * n, np.float32)
+    synth.adamw_w(n, out=host[:n])
+    synth.adamw_m(n, out=host[n:2 * n])
+    synth.adamw_v(n, out=host[2 * n:])
+    state0 = torch.from_numpy(host).to(dev)
+    del host
+    g = torch.from_numpy(synth.adamw_g()).to(dev)
+    st = torch.empty_like(state0)
+    ws = br.hash_workspace(3 * n, dev)
+    dg = torch.empty(32, dtype=torch.uint8, device=dev)
+    hp = dict(lr=cfg["lr"], beta1=cfg["beta1"], beta2=cfg["beta2"], eps=cfg["eps"], weight_decay=cfg["wd"],
+              step=cfg["step"])
+    for r in runs:
+        st.copy_(state0)
+        br.repro_adamw_hash(st, g, dg, ws, **hp)
+        r["adamw_hash_digest"] = bytes(dg.cpu().numpy()).hex()
+        r["adamw_state"] = _digest(st, ws)
+    stage("done")
+    out["runs"] = runs
+    print(json.dumps(out), flush=True)
+
+
 if __name__ == "__main__":
-    main()
+    main_full() if "--full" in sys.argv[1:] else main()

@@ -73,3 +73,34 @@ def test_two_processes_ten_runs_each_agree_with_the_oracle():
         oracle.adamw_bf16_step(w, m, v, gb, state, **C.BF16_HP)
     assert runs[0]["bf16_w"] == hashlib.sha256(w.tobytes()).hexdigest()
     assert runs[0]["bf16_m"] == _sha(m)
+
+
+_FULL = {}
+
+
+@pytest.mark.parametrize("which", ["first", "second"])
+def test_full_size_workloads_two_processes_ten_runs_each(which):
+    # The four full-size workloads (TreeFold 8 x 16,777,216; forward GEMM
+    # 8192 x 2048 x 8192; weight gradient with K = 16,384; the fused AdamW +
+    # state hash on the 1.2e9-parameter state), ten runs in each of two fresh
+    # processes.  Every run of every workload gives one state hash, in both
+    # processes; the reduce's also equals the oracle's.  (Sampled oracle rows
+    # and columns of the GEMMs and the oracle's digest of the updated state
+    # are checked in the per-op tests.)
+    print(f"full-size child process ({which})", flush=True)
+    res = subprocess.run([sys.executable, CHILD, "--full"], capture_output=True, text=True, timeout=600)
+    assert res.returncode == 0, res.stderr[-2000:]
+    _FULL[which] = json.loads(res.stdout.strip().splitlines()[-1])
+    runs = _FULL[which]["runs"]
+    assert len(runs) == 10
+    for r in runs[1:]:
+        assert r == runs[0]
+    assert runs[0]["adamw_hash_digest"] == runs[0]["adamw_state"]
+    if which == "first":
+        big = [synth.reduce_replica(r) for r in range(synth.REDUCE["R"])]
+        assert runs[0]["reduce"] == oracle.state_hash(oracle.tree_reduce(big)).hex()
+        return
+    first = _FULL.get("first")
+    assert first is not None, "the first full-size child did not run"
+    assert first["pid"] != _FULL["second"]["pid"]
+    assert first["runs"][0] == runs[0]

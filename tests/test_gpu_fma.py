@@ -70,6 +70,67 @@ def test_single_step_matches_oracle(unit):
         assert_bitwise(got, ref, f"unit {unit} set {si}")
 
 
+def _product_sets(seed, n):
+    """Operand pairs for the bare product: flush boundary, exact ties,
+    subnormal operands against large ones, overflow, and random exponents."""
+    rng = np.random.default_rng(seed)
+    sign = lambda: rng.choice([-1.0, 1.0], n)
+    sets = {}
+    # a * b within a few ulps of 2^-126 on both sides: mantissas near 1 and
+    # just below 2, at 2^-63; includes products that round up to 2^-126.
+    def near(lo):
+        k = rng.integers(1, 10, n)
+        top = rng.random(n) < 0.5
+        m = np.where(top, 2.0 - k * 2.0 ** -23, 1.0 + (k - 5) * 2.0 ** -23)
+        return (m * 2.0 ** np.where(top, lo - 1, lo) * sign()).astype(np.float32)
+    sets["boundary"] = (near(-63), near(-63))
+    # Exact ties at 24 bits: (1 + i 2^-12)(1 + j 2^-12) with i j odd.
+    i = 2 * rng.integers(0, 2000, n) + 1
+    j = 2 * rng.integers(0, 2000, n) + 1
+    e = rng.integers(-60, 60, n)
+    sets["ties"] = (((1 + i * 2.0 ** -12) * 2.0 ** e * sign()).astype(np.float32),
+                    ((1 + j * 2.0 ** -12) * 2.0 ** -e * sign()).astype(np.float32))
+    # Subnormal operands times large ones (normal if the operand were not
+    # read as zero), both orders.
+    sub = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-149, -127, n) * sign()).astype(np.float32)
+    big = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(20, 127, n) * sign()).astype(np.float32)
+    half = n // 2
+    sets["subnormal"] = (np.concatenate([sub[:half], big[half:]]), np.concatenate([big[:half], sub[half:]]))
+    # Overflow to infinity, and products just around the largest binary32.
+    a = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(60, 127, n) * sign()).astype(np.float32)
+    b = (rng.uniform(1, 2, n) * 2.0 ** rng.integers(60, 127, n) * sign()).astype(np.float32)
+    m = a[::2].size  # half the pairs land within a few ulps of the largest binary32, on both sides
+    a[::2] = (rng.uniform(1, 2, m) * 2.0 ** 64 * sign()[::2]).astype(np.float32)
+    fmax = float(np.finfo(np.float32).max)
+    b[::2] = (fmax / np.abs(a[::2].astype(np.float64)) * (1 + rng.integers(-6, 7, m) * 2.0 ** -24)
+              * sign()[::2]).astype(np.float32)
+    sets["overflow"] = (a, b)
+    # Random exponents over the whole range.
+    sets["random"] = ((rng.uniform(1, 2, n) * 2.0 ** rng.integers(-126, 64, n) * sign()).astype(np.float32),
+                      (rng.uniform(1, 2, n) * 2.0 ** rng.integers(-64, 64, n) * sign()).astype(np.float32))
+    z = np.array([0.0, -0.0, 1.0, -1.0, 2.0 ** -126, -(2.0 ** -126), 2.0 ** -140], np.float32)
+    g = np.array(np.meshgrid(z, z)).reshape(2, -1).astype(np.float32)
+    sets["zeros"] = (g[0], g[1])
+    return {k: (np.ascontiguousarray(a), np.ascontiguousarray(b)) for k, (a, b) in sets.items()}
+
+
+@pytest.mark.parametrize("unit", UNITS)
+def test_step_with_negative_zero_is_the_product(unit):
+    # With C = -0 (the identity of IEEE addition, which keeps a zero
+    # product's sign) a single step is the bare product fl(a * b) under the
+    # contract, bit for bit, on every unit.  The unfused GEMM's variant 3 takes
+    # its products from v_mfma_f32_32x32x1_2b_f32 (unit 1) this way.
+    for name, (a, b) in _product_sets(300 + unit, 100_003).items():
+        ref = oracle.fp32_op(oracle.OP_MUL, a, b)
+        if name == "overflow":
+            assert np.isinf(ref).sum() > a.size // 4 and (np.abs(ref[np.isfinite(ref)]) > 3e38).sum() > a.size // 8
+        if name == "boundary":
+            assert (ref == 0).any() and (np.abs(ref) == np.float32(2.0 ** -126)).any()
+        c = np.full(a.size, -0.0, np.float32)
+        got = to_host(br.repro_fp32_fma(to_dev(a), to_dev(b), to_dev(c), unit=unit))
+        assert_bitwise(got, ref, f"unit {unit} products {name}")
+
+
 @pytest.mark.parametrize("unit", [1, 2, 3])
 @pytest.mark.parametrize("n", [1, 63, 64, 65, 130, 4097])
 def test_mfma_unit_ragged_groups(n, unit):

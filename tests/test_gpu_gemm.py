@@ -101,16 +101,73 @@ def test_leading_dimensions_and_unaligned_views():
     assert (rest == 0).all()
 
 
-def test_subnormal_operands_and_products():
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_subnormal_operands_and_products(variant):
     # Subnormal inputs read as zero; products below 2^-126 flush; the chain's
-    # exact subnormal sums flush.  Compared with the oracle's rule.
+    # exact subnormal sums flush.  Compared with the oracle's rule, for every
+    # variant (variant 3 forms the products on the matrix cores).
     rng = np.random.default_rng(5)
     M, N, K = 32, 32, 40
     A = (rng.standard_normal((M, K)) * 2.0 ** -63).astype(np.float32)
     B = (rng.standard_normal((K, N)) * 2.0 ** -63).astype(np.float32)
     A[::3, ::2] = np.float32(2.0 ** -130)
     ref = oracle.gemm(A, B)
-    assert_bitwise(to_host(br.repro_gemm(to_dev(A), to_dev(B))), ref, "subnormal products")
+    assert_bitwise(to_host(br.repro_gemm(to_dev(A), to_dev(B), variant=variant)), ref,
+                   f"subnormal products variant={variant}")
+
+
+def _boundary_operands(rng, rows, cols):
+    """Operands whose pairwise products sit on the flush boundary: mantissas
+    within a few ulps of 1 (and of 2) times 2^-63, both signs, so that a * b
+    lands within ulps of 2^-126 on either side; plus exact zeros of both signs,
+    subnormals and the smallest normal."""
+    k = rng.integers(-4, 5, (rows, cols))
+    top = rng.random((rows, cols)) < 0.5
+    mant = np.where(top, 2.0 - (k + 5) * 2.0 ** -23, 1.0 + k * 2.0 ** -23)
+    x = mant * 2.0 ** np.where(top, -64, -63) * rng.choice([-1.0, 1.0], (rows, cols))
+    special = np.array([0.0, -0.0, 2.0 ** -149, -(2.0 ** -140), 2.0 ** -126, -(2.0 ** -126)])
+    mask = rng.random((rows, cols)) < 0.15
+    x = np.where(mask, special[rng.integers(0, special.size, (rows, cols))], x)
+    return x.astype(np.float32)
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_directed_flush_boundary_products(variant):
+    # Every product a * b is within a few ulps of +-2^-126 (or a zero or
+    # subnormal operand), so each step's product is decided by the flush rule:
+    # tiny after rounding -> signed zero, otherwise the rounded product.  The
+    # chain then adds values of a few times 2^-126, whose exact sums are normal
+    # or flush.  One GEMM per variant against the oracle, plus the K = 1 case
+    # where every output is a single product.
+    rng = np.random.default_rng(11)
+    for M, N, K in ((64, 64, 1), (96, 80, 37), (130, 129, 64)):
+        A = _boundary_operands(rng, M, K)
+        B = _boundary_operands(rng, K, N)
+        ref = oracle.gemm(A, B)
+        got = to_host(br.repro_gemm(to_dev(A), to_dev(B), variant=variant))
+        assert_bitwise(got, ref, f"{M}x{N}x{K} boundary variant={variant}")
+        # The set really straddles the boundary: some products flush, some survive.
+        p = oracle.fp32_op(oracle.OP_MUL, np.repeat(A[:, :1], N, 1).reshape(-1), np.tile(B[0], M))
+        assert (p == 0).any() and (np.abs(p) >= np.float32(2.0 ** -126)).any()
+
+
+@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+def test_overflowing_products(variant):
+    # A product beyond the largest binary32 rounds to infinity of its sign and
+    # stays there along the chain; the other outputs stay finite.
+    M, N, K = 70, 66, 33
+    rng = np.random.default_rng(12)
+    A = rng.standard_normal((M, K)).astype(np.float32)
+    B = rng.standard_normal((K, N)).astype(np.float32)
+    A[5, 7] = np.float32(2.0 ** 100)
+    B[7, :] = (np.where(np.arange(N) % 2 == 0, 1.0, -1.0) * 2.0 ** 60).astype(np.float32)
+    A[9, 3] = np.float32(-(2.0 ** 127))
+    B[3, ::3] = np.float32(1.5)
+    ref = oracle.gemm(A, B)
+    assert np.isposinf(ref[5, 0]) and np.isneginf(ref[5, 1]) and np.isneginf(ref[9, 0])
+    assert np.isnan(ref).sum() == 0
+    got = to_host(br.repro_gemm(to_dev(A), to_dev(B), variant=variant))
+    assert_bitwise(got, ref, f"overflow variant={variant}")
 
 
 def _sampled_check(C, A, B, ta, tb, rows, cols, what):
@@ -130,9 +187,21 @@ def _sampled_check(C, A, B, ta, tb, rows, cols, what):
         assert_bitwise(C[:, c], ref[:, 0], f"{what} column {c}")
 
 
+def _repeat_digests(run, out, times=10):
+    """State hashes (computed on the GPU) of `out` after each of `times` runs."""
+    ws = br.hash_workspace(out.numel(), out.device)
+    digests = []
+    for _ in range(times):
+        out.fill_(7.0)
+        run()
+        digests.append(br.repro_state_hash(out.reshape(-1), ws))
+    return digests
+
+
 def test_forward_workload_full_size_sampled():
     # Y[8192 x 8192] = X[8192 x 2048] W[2048 x 8192], K = 2048.  Full rows and
-    # columns at tile edges and at random positions; ten repeats identical.
+    # columns at tile edges and at random positions; ten runs give one digest
+    # of the whole output.
     cfg = synth.GEMM
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     print(f"gemm workload {M}x{N}x{K}", flush=True)
@@ -145,26 +214,32 @@ def test_forward_workload_full_size_sampled():
     rows = [0, 127, 128, 4095, M - 1] + rng.integers(0, M, 3).tolist()
     cols = [0, 127, 128, N - 1] + rng.integers(0, N, 2).tolist()
     _sampled_check(C, X, W, False, False, rows, cols, "gemm workload")
-    first = Y.clone()
-    for _ in range(3):
-        again = br.repro_gemm(dX, dW)
-        assert torch.equal(again.view(torch.int32), first.view(torch.int32))
+    first = br.repro_state_hash(Y.reshape(-1))
+    digests = _repeat_digests(lambda: br.repro_gemm(dX, dW, out=Y), Y)
+    assert digests == [first] * 10
+    assert np.array_equal(to_host(Y).view(np.uint32), C.view(np.uint32))
 
 
 def test_weight_gradient_workload_full_size_sampled():
     # dW[2048 x 8192] = X^T dY with X[16384 x 2048], dY[16384 x 8192]: one
-    # 16,384-long ascending chain per output; heavy-tailed t(3) data.
+    # 16,384-long ascending chain per output; heavy-tailed t(3) data.  Ten
+    # runs give one digest of the whole output.
     cfg = synth.DW
     M, N, K = cfg["M"], cfg["N"], cfg["K"]
     print(f"dW workload {M}x{N}x{K}", flush=True)
     X = synth.dw_x().reshape(K, M)
     dY = synth.dw_dy().reshape(K, N)
-    out = br.repro_gemm(to_dev(X), to_dev(dY), trans_a=True)
+    dX, ddY = to_dev(X), to_dev(dY)
+    out = br.repro_gemm(dX, ddY, trans_a=True)
     C = to_host(out)
     rng = np.random.default_rng(4)
     rows = [0, 128, M - 1] + rng.integers(0, M, 1).tolist()
     cols = [0, 255, N - 1] + rng.integers(0, N, 1).tolist()
     _sampled_check(C, X, dY, True, False, rows, cols, "dW workload")
+    first = br.repro_state_hash(out.reshape(-1))
+    digests = _repeat_digests(lambda: br.repro_gemm(dX, ddY, trans_a=True, out=out), out)
+    assert digests == [first] * 10
+    assert np.array_equal(to_host(out).view(np.uint32), C.view(np.uint32))
 
 
 def test_errors():

@@ -18,7 +18,7 @@ sys.path.insert(0, __import__("os").path.join(__import__("os").path.dirname(__fi
                                                "bitwise_reproducible_amd", "csrc"))
 import build as lib_build  # noqa: E402
 
-SOURCES = ["gemm.hip", "elementwise.hip", "replay.hip", "state_hash.hip", "fused.hip"]
+SOURCES = ["gemm.hip", "elementwise.hip", "replay.hip", "state_hash.hip", "fused.hip", "optimizer.hip"]
 FUSED_OR_PACKED = re.compile(r"^v_(fma|fmac|mac|mad)_f32|^v_pk_(fma|add|mul)_f32|^v_(fma|mad)_mix|^v_fma_legacy")
 # Kernels of the declared fused convention.
 FUSED_KERNELS = ("k_gemm_fma", "k_gemm_mfma_fma", "k_fma_valu", "k_fma_mfma")
@@ -71,7 +71,7 @@ def test_only_fused_convention_kernels_fuse(kernels):
         fused = sum(c for op, c in ops.items() if FUSED_OR_PACKED.match(op))
         allowed = 5 * (ops["v_div_fixup_f32"] + ops["v_rsq_f32_e32"])
         assert fused <= allowed, f"{_short(name)} ({name}): {fused} fused instructions, {allowed} allowed"
-        if _short(name).startswith(("k_gemm", "k_tree_reduce", "k_replay", "k_fold", "k_hash")):
+        if _short(name).startswith(("k_gemm", "k_tree_reduce", "k_replay", "k_fold", "k_hash", "k_norm_fold")):
             assert fused == 0, f"{_short(name)} has fused instructions"
 
 
