@@ -162,7 +162,7 @@ def test_overflowing_products(variant):
     A[5, 7] = np.float32(2.0 ** 100)
     B[7, :] = (np.where(np.arange(N) % 2 == 0, 1.0, -1.0) * 2.0 ** 60).astype(np.float32)
     A[9, 3] = np.float32(-(2.0 ** 127))
-    B[3, ::3] = np.float32(1.5)
+    B[3, ::3] = np.float32(4.0)  # -2^127 * 4 = -2^129: beyond the largest binary32
     ref = oracle.gemm(A, B)
     assert np.isposinf(ref[5, 0]) and np.isneginf(ref[5, 1]) and np.isneginf(ref[9, 0])
     assert np.isnan(ref).sum() == 0
