@@ -16,6 +16,7 @@ Entry points (same names as the C ABI):
     repro_state_hash_async(words, digest_out, workspace)
     repro_fp32_ops(op, a, b, out=None);  repro_fp32_fma(a, b, c, unit=0, out=None)
     repro_adamw_hash(state, grad, digest_out, workspace, lr, beta1, beta2, eps, weight_decay, step, chunk=0)
+    repro_adamw_hash_noalloc(state, grad, digest_out, lr, beta1, beta2, eps, weight_decay, step)
     repro_grad_norm(grad, workspace=None, out=None) -> device tensor [norm, S]
     repro_adamw_bf16_step(w, m, v, grad, state, lr, beta1, beta2, eps, weight_decay,
                           max_norm=1.0, spike_threshold=5.0, skip_steps=5, workspace=None)
@@ -78,10 +79,12 @@ def library():
         lib.repro_adamw_bf16_step.argtypes = [vp, vp, vp, vp, i32, i64, f32, f32, f32, f32, f32, f32, f32, i32, vp,
                                               i64, vp, vp]
         lib.repro_fp32_fma.argtypes = [vp, vp, vp, vp, i64, i32, vp]
+        lib.repro_adamw_hash_noalloc.argtypes = [vp, vp, i64, f32, f32, f32, f32, f32, i64, vp, vp]
         for name in ("repro_gemm", "repro_gemm_variant", "repro_tree_reduce", "repro_tree_reduce_variant",
                      "repro_adamw", "repro_adamw_variant", "repro_state_hash", "repro_fp32_ops",
                      "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_gemm_fma",
-                     "repro_fp32_fma", "repro_grad_norm", "repro_adamw_bf16_step", "repro_adamw_hash"):
+                     "repro_fp32_fma", "repro_grad_norm", "repro_adamw_bf16_step", "repro_adamw_hash",
+                     "repro_adamw_hash_noalloc"):
             getattr(lib, name).restype = ctypes.c_int
         _lib = lib
     return _lib
@@ -342,6 +345,25 @@ def repro_adamw_hash(state, grad, digest_out, workspace, lr: float, beta1: float
                                       int(chunk), _stream(stream)), "repro_adamw_hash")
 
 
+REPRO_NOALLOC_SCRATCH_BYTES = 128 << 20
+
+
+def repro_adamw_hash_noalloc(state, grad, digest_out, lr: float, beta1: float, beta2: float, eps: float,
+                             weight_decay: float, step: int, stream=None):
+    """repro_adamw_hash without a workspace: the library's per-device array holds the digests
+    (calls overlapping on one device race; see repro.h)."""
+    import torch
+    _on_device(state, "state", torch.float32)
+    _on_device(grad, "grad", torch.float32)
+    _on_device(digest_out, "digest_out", torch.uint8, 32)
+    n = grad.numel()
+    if state.numel() != 3 * n:
+        raise ValueError("state must hold 3n floats for a grad of n")
+    _check(library().repro_adamw_hash_noalloc(state.data_ptr(), grad.data_ptr(), n, lr, beta1, beta2, eps,
+                                              weight_decay, int(step), digest_out.data_ptr(), _stream(stream)),
+           "repro_adamw_hash_noalloc")
+
+
 def repro_fp32_ops(op: int, a, b=None, out=None, stream=None):
     """One contract operation per element (diagnostic; see repro.h)."""
     import torch
@@ -447,7 +469,7 @@ def repro_adamw_bf16_step(w, m, v, grad, state, lr: float, beta1: float, beta2: 
                                            state.data_ptr(), _stream(stream)), "repro_adamw_bf16_step")
 
 
-__all__ = ["repro_gemm", "repro_adamw_hash", "repro_grad_norm", "repro_adamw_bf16_step", "new_step_state", "read_step_state",
+__all__ = ["repro_gemm", "repro_adamw_hash", "repro_adamw_hash_noalloc", "REPRO_NOALLOC_SCRATCH_BYTES", "repro_grad_norm", "repro_adamw_bf16_step", "new_step_state", "read_step_state",
            "grad_norm_workspace", "repro_gemm_fma", "repro_fp32_fma", "repro_tree_reduce", "repro_replay_reduce", "repro_fold_push", "repro_fold_result", "repro_adamw", "repro_state_hash", "repro_state_hash_async",
            "repro_state_hash_workspace_bytes", "repro_fp32_ops", "hash_workspace", "spec_version", "library",
            "ReproError", "LIB_PATH"]

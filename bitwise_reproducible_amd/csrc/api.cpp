@@ -14,8 +14,9 @@
 
 // The host-side scalars below change the SSE control register around their
 // arithmetic; declaring access to the floating-point environment keeps the
-// compiler from moving that arithmetic across the change.  (This file has no
-// device code; the device pass does not know the pragma.)
+// compiler from moving that arithmetic across the change.  (The device pass,
+// which sees only the no-allocation workspace array below, does not know the
+// pragma.)
 #ifndef __HIP_DEVICE_COMPILE__
 #pragma STDC FENV_ACCESS ON
 #endif
@@ -326,6 +327,66 @@ int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float
     if ((e = hipStreamWaitEvent(main, joined, 0)) != hipSuccess) return status_of(e);
   }
   return status_of(repro::launch_hash_upper(ws, plan, digest_out, main));
+}
+
+namespace {
+
+// Workspace of repro_adamw_hash_noalloc: one array per device, placed by the
+// code-object loader, so the call needs no allocation of any kind.  In host
+// code the name `scratch` is only a stand-in for the symbol; the device
+// address comes from hipGetSymbolAddress, once per device, and only that
+// address is ever handed to a kernel.
+static __device__ __align__(256) uint8_t scratch[REPRO_NOALLOC_SCRATCH_BYTES];
+
+std::mutex g_scratch_mutex;
+void* g_scratch_ptr[kMaxDevices] = {};
+
+// The device address of the current device's `scratch`, looked up on the
+// first call made on that device.
+hipError_t scratch_address(void** out) {
+  int device = 0;
+  hipError_t e = hipGetDevice(&device);
+  if (e != hipSuccess) return e;
+  if (device < 0 || device >= kMaxDevices) return hipErrorInvalidDevice;
+  std::lock_guard<std::mutex> lock(g_scratch_mutex);
+  if (g_scratch_ptr[device] == nullptr) {
+    void* p = nullptr;
+    e = hipGetSymbolAddress(&p, HIP_SYMBOL(scratch));
+    if (e != hipSuccess) return e;
+    if (p == nullptr || (reinterpret_cast<uintptr_t>(p) & 255u) != 0) return hipErrorInvalidSymbol;
+    g_scratch_ptr[device] = p;
+  }
+  *out = g_scratch_ptr[device];
+  return hipSuccess;
+}
+
+}  // namespace
+
+int repro_adamw_hash_noalloc(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2,
+                             float eps, float weight_decay, int64_t step, uint8_t* digest_out, void* stream) {
+  if (n < 0 || step < 1 || digest_out == nullptr) return REPRO_EINVAL;
+  if (n > 0 && (state == nullptr || grad == nullptr)) return REPRO_EINVAL;
+  if (n > 0 && (!aligned4(state) || !aligned4(grad))) return REPRO_EALIGN;
+  if ((reinterpret_cast<uintptr_t>(digest_out) & 15u) != 0) return REPRO_EALIGN;
+  if (n > INT64_MAX / 3) return REPRO_ESPACE;
+  repro::HashPlan plan;
+  repro::plan_state_hash(3 * n, &plan);
+  if (plan.total_bytes > REPRO_NOALLOC_SCRATCH_BYTES) return REPRO_ESPACE;
+  void* ws = nullptr;
+  const hipError_t e = scratch_address(&ws);
+  if (e != hipSuccess) return status_of(e);
+  const hipStream_t main = static_cast<hipStream_t>(stream);
+  const AdamwScalars s = adamw_scalars(lr, beta1, beta2, eps, weight_decay, step);
+  uint8_t* wsb = static_cast<uint8_t*>(ws);
+  const bool al16 = ((reinterpret_cast<uintptr_t>(state) | reinterpret_cast<uintptr_t>(grad)) & 15u) == 0;
+  if (n > 0 && n % kLeafWords == 0 && al16)
+    return status_of(repro::launch_adamw_hash_fused(state, grad, n, s, wsb, plan, digest_out, main));
+  // Otherwise the update and then the hash, both on the caller's stream.
+  if (n > 0) {
+    const hipError_t e2 = repro::launch_adamw(state, grad, n, s, 0, main);
+    if (e2 != hipSuccess) return status_of(e2);
+  }
+  return status_of(repro::launch_state_hash(state, 3 * n, wsb, plan, digest_out, main));
 }
 
 int64_t repro_state_hash_workspace_bytes(int64_t n_words) {

@@ -35,7 +35,10 @@
  *   - The caller owns every buffer.  The library allocates no device memory.
  *     Its only global state is a pair of streams and a pool of events per
  *     device, created by the first repro_adamw_hash call with chunk > 0 and
- *     kept until the process ends.  Calls are thread-safe.
+ *     kept until the process ends, and the workspace array of
+ *     repro_adamw_hash_noalloc (one per device, see there).  Calls are
+ *     thread-safe, except that repro_adamw_hash_noalloc calls overlapping on
+ *     one device share that array.
  *   - `stream` is a hipStream_t passed as void* (NULL = the null stream).
  *     Every call only enqueues work on it and returns without waiting.
  *   - Return value: REPRO_OK (0) or a negative REPRO_E* code.  On an error
@@ -358,6 +361,35 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
 int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2, float eps,
                      float weight_decay, int64_t step, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
                      int64_t chunk, void* stream);
+
+/*
+ * repro_adamw_hash_noalloc: repro_adamw_hash (chunk == 0) for callers that
+ * cannot allocate device memory: code under HIP graph capture, tight
+ * serving loops, or harnesses that forbid allocation.  Same update, same
+ * digest, bit for bit, with no workspace argument.
+ *
+ * The hash digests of every level live in a device array that the library
+ * holds on each device it runs on (REPRO_NOALLOC_SCRATCH_BYTES, placed when
+ * the library's code is loaded onto that device and kept until the process
+ * ends); the call allocates nothing, frees nothing and creates no stream or
+ * event.  Nothing in the array needs to start at zero: every digest slot is
+ * written before it is read.  All calls on one device share that array, so
+ * calls that overlap in time on one device (concurrent streams, or host
+ * threads on different streams) race and must be serialised by the caller,
+ * e.g. by using one stream.
+ *
+ *   state, grad, n, lr ... step: as repro_adamw.  With n a multiple of 1024
+ *          and 16-byte aligned state and grad, one kernel updates and hashes
+ *          the leaves; otherwise the update and then the hash run in turn on
+ *          the caller's stream.
+ *   digest_out: device pointer to 32 bytes (16-byte aligned).
+ * REPRO_ESPACE when the hash of 3n words needs more than the array holds
+ * (repro_state_hash_workspace_bytes(3n) > REPRO_NOALLOC_SCRATCH_BYTES, i.e.
+ * n above about 1.34e9); nothing is enqueued then.  Asynchronous.
+ */
+#define REPRO_NOALLOC_SCRATCH_BYTES (128LL << 20)
+int repro_adamw_hash_noalloc(float* state, const float* grad, int64_t n, float lr, float beta1, float beta2,
+                             float eps, float weight_decay, int64_t step, uint8_t* digest_out, void* stream);
 
 /*
  * repro_fp32_ops: one contract operation per element, out[i] = a[i] op b[i],

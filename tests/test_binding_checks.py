@@ -28,6 +28,9 @@ CASES = {
                                                                 _host(4096, torch.uint8)),
     "repro_adamw_hash": lambda: br.repro_adamw_hash(_host(3 * 1024), _host(), _host(32, torch.uint8),
                                                     _host(4096, torch.uint8), 1e-3, 0.9, 0.999, 1e-8, 0.1, 1),
+    "repro_adamw_hash_noalloc": lambda: br.repro_adamw_hash_noalloc(_host(3 * 1024), _host(),
+                                                                    _host(32, torch.uint8), 1e-3, 0.9, 0.999,
+                                                                    1e-8, 0.1, 1),
     "repro_fp32_ops": lambda: br.repro_fp32_ops(0, _host(), _host()),
     "repro_fp32_fma": lambda: br.repro_fp32_fma(_host(), _host(), _host()),
     "repro_grad_norm": lambda: br.repro_grad_norm(_host(), workspace=_host(4096, torch.uint8),
