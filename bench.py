@@ -46,18 +46,29 @@ FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
 # the same rate (measured), which bounds the hash.
 VALU_LANE_OPS = 256 * 128 * 2.4e9
 GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
-# BLAKE2b: per 128-byte block 12 rounds x 8 G.  In issue slots of the
-# 32-bit VALU: a G is 6 64-bit adds (v_add_co + v_addc, 2 slots each), 4
-# 64-bit xors (2 slots each) and 3 rotations by 24/16/63 (two v_alignbit_b32
-# each; 3-operand VOP3 ops issue at half rate on gfx950, measured, so 4
-# slots); the rotation by 32 is a register swap.  32 slots per G, plus 16
-# xors of the feed-forward: 3088 slots per 128 bytes.
-HASH_SLOTS_PER_BYTE = (12 * 8 * 32 + 16) / 128
-HASH_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
-# The AdamW update: 170 VALU instructions per four elements in the compiled
-# kernel (16 operations each, with the correctly rounded division and square
-# root sequences), about 42 issue slots per element.
-ADAMW_SLOTS_PER_ELEMENT = 42
+# BLAKE2b: per 128-byte block 12 rounds x 8 G.  The compiled compression
+# (k_hash_leaves, gfx950) is 2001 VALU instructions: 802 v_xor_b32 and 46
+# other 4-byte ones, 577 v_lshl_add_u64 (one per 64-bit add) and 576
+# v_alignbit_b32 (two per rotation by 24, 16 or 63); the rotation by 32 is a
+# register swap.  The instruction audit in the tests checks these counts.
+HASH_VALU_PER_BLOCK = 2001
+HASH_VALU_8BYTE_PER_BLOCK = 1153   # v_lshl_add_u64 + v_alignbit_b32: 8-byte (VOP3) encodings
+# Bound 1 (the `peak` of the hash rows): one issue slot per VALU instruction
+# at the VALU issue rate above.
+HASH_INSTR_PER_BYTE = HASH_VALU_PER_BLOCK / 128
+HASH_PEAK_GBS = VALU_LANE_OPS / HASH_INSTR_PER_BYTE / 1e9
+# Bound 2 (reported beside it as `*_issue_model`): an 8-byte encoding takes
+# two issue slots.  This is an assumption about gfx950's issue, supported by
+# the kernels' own counters: the unfused GEMM (4-byte VALU instructions only)
+# issues 0.39-0.42 wave-instructions per SIMD per clock and the leaf hash
+# (58% 8-byte) 0.255, which that rule predicts (0.27).
+HASH_SLOTS_PER_BYTE = (HASH_VALU_PER_BLOCK + HASH_VALU_8BYTE_PER_BLOCK) / 128
+HASH_MODEL_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
+# The AdamW update in the fused kernel: 190 VALU instructions per four
+# elements (16 operations each, with the correctly rounded division and
+# square-root sequences), 47.5 per element, all 4-byte encodings but the
+# division's v_div_scale / v_div_fmas / v_div_fixup and a few fma.
+ADAMW_INSTR_PER_ELEMENT = 47.5
 
 
 def recorded_traffic():
@@ -97,6 +108,10 @@ def parse():
     p.add_argument("--warmup", type=int, default=3)
     p.add_argument("--no-verify", action="store_true", help="skip the oracle check after timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
+    p.add_argument("--gemm-variants", action="store_true",
+                   help="only the forward GEMM workload, once each with repro_gemm variant 0 (VALU), variant 3 "
+                        "(matrix-core products, VALU adds) and repro_gemm_fma variant 0 (matrix cores), after one "
+                        "warm-up each: the run the matrix-core co-execution counters are taken on")
     p.add_argument("--calibration-copy", action="store_true",
                    help="after timing, run one plain copy of 64 MiB (a one-replica fold without the average) whose "
                         "HBM counters calibrate the FETCH_SIZE / WRITE_SIZE readings of a profiling run")
@@ -141,6 +156,9 @@ def main():
 
     dev = torch.device("cuda:0")
     torch.cuda.set_device(dev)
+    if args.gemm_variants:
+        gemm_variants(torch, np, br, synth, dev)
+        return
     up = Upload(torch)
     t_setup = time.time()
 
@@ -364,6 +382,11 @@ def main():
     flops_dw = 2 * DC["M"] * DC["N"] * DC["K"]
     mem_ms = op_ms["tree_reduce"] + op_ms["adamw_state_hash"]
     value = (bytes_reduce + bytes_adamw + bytes_hash) / (mem_ms * 1e-3) / 1e9
+    # The bytes of those two ops that cross HBM: the reduce's, the update's
+    # 28n and the leaf and inner digests written (the fused kernel hashes the
+    # updated state from LDS, so the 12n hashed bytes are not read again).
+    bytes_digests = br.repro_state_hash_workspace_bytes(3 * n)
+    hbm_gbps = (bytes_reduce + bytes_adamw + bytes_digests) / (mem_ms * 1e-3) / 1e9
     gemm_ms = op_ms["gemm_fwd"] + op_ms["gemm_dw"]
     gemm_gflops = (flops_fwd + flops_dw) / (gemm_ms * 1e-3) / 1e9
 
@@ -375,22 +398,29 @@ def main():
                     "unit": "TFLOP/s", "frac": round(ach / GEMM_PEAK_TFLOPS, 4), "traffic": None,
                     "frac_of_fp32_vector_peak": round(ach / FP32_VECTOR_PEAK, 4)}
         if op == "adamw_state_hash":
-            # One kernel, bound by the tighter of HBM (28n bytes) and the
-            # VALU issue of the hash plus the update (slots per element).
+            # One kernel, bound by the tighter of HBM (28n bytes) and the VALU
+            # issue of the hash plus the update (instructions per element).
             t_hbm = bytes_adamw / (HBM_PEAK_GBS * 1e9)
-            t_alu = n * (12 * HASH_SLOTS_PER_BYTE + ADAMW_SLOTS_PER_ELEMENT) / VALU_LANE_OPS
-            peak = bytes_hash / max(t_hbm, t_alu) / 1e9
+            t_alu = n * (12 * HASH_INSTR_PER_BYTE + ADAMW_INSTR_PER_ELEMENT) / VALU_LANE_OPS
+            t_model = n * (12 * HASH_SLOTS_PER_BYTE + ADAMW_INSTR_PER_ELEMENT) / VALU_LANE_OPS
+            t_bound = max(t_hbm, t_alu)
+            peak = bytes_hash / t_bound / 1e9
             ach = bytes_hash / (ms * 1e-3) / 1e9
             return {"bound": "alu" if t_alu >= t_hbm else "hbm", "achieved": round(ach, 1), "peak": round(peak, 1),
-                    "unit": "GB/s (of state hashed)", "frac": round(ach / peak, 4), "traffic": None,
+                    "unit": "GB/s (of state hashed)", "frac": round(t_bound / (ms * 1e-3), 4), "traffic": None,
+                    "bound_ms": {"hbm": round(t_hbm * 1e3, 3), "alu_one_slot": round(t_alu * 1e3, 3),
+                                 "alu_issue_model": round(t_model * 1e3, 3)},
+                    "frac_issue_model": round(max(t_hbm, t_model) / (ms * 1e-3), 4),
                     "hbm_achieved": round(bytes_adamw / (ms * 1e-3) / 1e9, 1),
                     "frac_of_hbm_peak": round(bytes_adamw / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
                     "hbm_frac_of_copy": round(bytes_adamw / (ms * 1e-3) / 1e9 / copy_gbps, 4)}
         b = {"tree_reduce": bytes_reduce, "adamw": bytes_adamw, "state_hash": bytes_hash}[op]
         ach = b / (ms * 1e-3) / 1e9
-        if op == "state_hash":  # integer-VALU bound: ~24 issue slots per byte
+        if op == "state_hash":  # integer-VALU bound: 15.6 instructions per byte
             return {"bound": "alu", "achieved": round(ach, 1), "peak": round(HASH_PEAK_GBS, 1), "unit": "GB/s",
                     "frac": round(ach / HASH_PEAK_GBS, 4), "traffic": None,
+                    "peak_issue_model": round(HASH_MODEL_PEAK_GBS, 1),
+                    "frac_issue_model": round(ach / HASH_MODEL_PEAK_GBS, 4),
                     "frac_of_hbm_peak": round(ach / HBM_PEAK_GBS, 4)}
         return {"bound": "hbm", "achieved": round(ach, 1), "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(ach / HBM_PEAK_GBS, 4), "traffic": None, "frac_of_copy": round(ach / copy_gbps, 4)}
@@ -434,6 +464,11 @@ def main():
         "config": {"workload": "reduce R=8 n=16777216; gemm 8192x2048 @ 2048x8192; adamw+state_hash n=1.2e9 "
                                "[w|m|v] 14.4 GB; dW 2048x8192 K=16384",
                    "parallelism": "none (1 GPU)"},
+        "value_counts": "algorithmic bytes of reduce + AdamW + hash: (R+1)*4n_reduce + 28n + 12n hashed, over the "
+                        "event time of the reduce and the fused AdamW + hash; the 12n hashed bytes are read from LDS, "
+                        "not HBM (see hbm_gbps)",
+        "hbm_gbps": round(hbm_gbps, 1),
+        "hbm_frac": round(hbm_gbps / HBM_PEAK_GBS, 4),
         "gemm": {"value": round(gemm_gflops, 1), "unit": "GFLOP/s"},
         "hbm_copy": {"gbps": round(copy_gbps, 1), "ms_median": round(copy_ms, 4), "bytes": 8 * copy_n,
                      "kernel": "k_tree_reduce_v4<1, false> (one-replica fold: a plain copy)"},
@@ -456,6 +491,30 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np)
     print(json.dumps(out), flush=True)
+
+
+def gemm_variants(torch, np, br, synth, dev):
+    """The forward GEMM workload through the unfused VALU kernel, the unfused
+    kernel with matrix-core products, and the fused matrix-core kernel."""
+    GC = synth.GEMM
+    X = torch.from_numpy(synth.gemm_x()).to(dev).view(GC["M"], GC["K"])
+    W = torch.from_numpy(synth.gemm_w()).to(dev).view(GC["K"], GC["N"])
+    Y = torch.empty(GC["M"], GC["N"], dtype=torch.float32, device=dev)
+    runs = {"repro_gemm_variant0": lambda: br.repro_gemm(X, W, out=Y, variant=0),
+            "repro_gemm_variant3": lambda: br.repro_gemm(X, W, out=Y, variant=3),
+            "repro_gemm_fma_variant0": lambda: br.repro_gemm_fma(X, W, out=Y, variant=0)}
+    out = {}
+    for name, call in runs.items():
+        call()
+        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+        e0.record()
+        call()
+        e1.record()
+        torch.cuda.synchronize()
+        out[name] = {"ms": round(e0.elapsed_time(e1), 4),
+                     "digest": br.repro_state_hash(Y.view(-1)).hex()}
+        log(name, out[name])
+    print(json.dumps({"gemm_variants": out, "workload": "gemm 8192x2048 @ 2048x8192"}), flush=True)
 
 
 def verify(torch, np, br, reps, g_red, X3, W3, Y3, X5, dY5, dW5, state, ws, n, aidx, samples, hp, step0, nsteps):
@@ -619,6 +678,12 @@ def cpu_baseline(np):
     g = synth.adamw_g(n_adam)
     x = synth.gemm_x(rows=16).reshape(16, 2048)
     bt = np.ascontiguousarray(synth.gemm_w().reshape(2048, 8192).T)
+    # The weight-gradient shape: 8 output rows of dW = X^T dY (K = 16,384
+    # terms per chain), i.e. 8 columns of X against dY, with dY transposed so
+    # that the oracle's k loop reads both operands contiguously.
+    dw_rows = 8
+    xw = np.ascontiguousarray(synth.dw_x().reshape(16384, 2048)[:, :dw_rows].T)
+    dyt = np.ascontiguousarray(synth.dw_dy().reshape(16384, 8192).T)
     # One thread on one core: the calling thread is pinned for the timed part.
     try:
         saved = os.sched_getaffinity(0)
@@ -635,13 +700,18 @@ def cpu_baseline(np):
     t3 = time.perf_counter()
     oracle.gemm(x, bt, trans_b=True)
     t4 = time.perf_counter()
+    oracle.gemm(xw, dyt, trans_b=True)
+    t5 = time.perf_counter()
     if saved is not None:
         os.sched_setaffinity(0, saved)
+    del xw, dyt
     nbytes = 9 * 4 * n_red + 28 * n_adam + 12 * n_adam
     return {"value": round(nbytes / (t3 - t0) / 1e9, 4), "unit": "GB/s", "cores": 1, "kind": "oracle",
             "gemm_gflops": round(2 * 16 * 8192 * 2048 / (t4 - t3) / 1e9, 4),
+            "gemm_dw_gflops": round(2 * dw_rows * 8192 * 16384 / (t5 - t4) / 1e9, 4),
             "sample": f"the reduce workload (R=8 n={n_red}) and 2/3 of the optimizer workload (adamw + state_hash "
-                      f"n={n_adam}); gemm: 16 rows of 8192x2048x8192; single-threaded oracle, {t4 - t0:.1f} s",
+                      f"n={n_adam}); gemm: 16 rows of 8192x2048x8192 and {dw_rows} rows of dW 2048x8192 "
+                      f"(K=16384); single-threaded oracle, {t5 - t0:.1f} s",
             "host_cpu": _cpu_model(), "host_threads": os.cpu_count(), "pinned_core": core}
 
 

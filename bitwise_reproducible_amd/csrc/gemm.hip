@@ -503,7 +503,11 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   if (variant == 2)
     return dispatch<64, 64, 16, 4, 4, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   if (variant == 3) return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  return dispatch<128, 128, 16, 8, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  // 32-deep k slabs: half the barriers and slab loads per MAC of 16-deep
+  // ones; measured on MI355X 2% faster on the weight-gradient workload and
+  // 1-10% on the forward one, same bits (213 and 249 VGPRs: still two waves
+  // per SIMD; 67.6 KB of LDS: two workgroups per CU).
+  return dispatch<128, 128, 32, 8, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 
 }  // namespace repro

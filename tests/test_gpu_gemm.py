@@ -45,7 +45,7 @@ def test_shapes_transposes_variants(M, N, K, ta, tb):
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_many_tiles_with_ragged_edges(ta, tb):
     # 1000 x 1500 x 700: 8 x 12 tiles of 128 with partial last tiles in M and
-    # N, and 43 full k-slabs of 16 plus a partial one, for every variant.
+    # N, and a partial last k-slab (21 of 32 plus 28; 43 of 16 plus 12), for every variant.
     M, N, K = 1000, 1500, 700
     A, B = _stored(M, N, K, ta, tb, 0x8800 + 2 * ta + tb)
     ref = oracle.gemm(A, B, bool(ta), bool(tb))

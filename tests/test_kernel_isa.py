@@ -103,10 +103,13 @@ def test_fused_kernels_use_the_declared_units(kernels):
 
 def test_unfused_gemm_chain_is_one_multiply_and_one_add_per_step(kernels):
     ks, _ = kernels
+    seen = 0
     for name, ops in ks.items():
-        if _short(name) == "k_gemm" and "Li128ELi128ELi16ELi8ELi8E" in name:
-            # 16 k steps x 8 x 8 outputs per lane in the unrolled slab loop.
-            assert ops["v_mul_f32_e32"] >= 1024 and ops["v_add_f32_e32"] >= 1024
+        if _short(name) == "k_gemm" and "Li128ELi128ELi32ELi8ELi8E" in name:
+            # 32 k steps x 8 x 8 outputs per lane in the unrolled slab loop.
+            assert ops["v_mul_f32_e32"] >= 2048 and ops["v_add_f32_e32"] >= 2048, ops
+            seen += 1
+    assert seen == 8  # the default kernel, 4 transposes x 2 load widths
 
 
 def test_no_kernel_uses_scratch(kernels):
@@ -114,3 +117,24 @@ def test_no_kernel_uses_scratch(kernels):
     assert set(meta) >= set(ks)
     spilled = {_short(k): v for k, v in meta.items() if v}
     assert not spilled, spilled
+
+
+def test_hash_compression_instruction_mix(kernels):
+    # The hash rows' bounds count ~2,000 VALU instructions per 128-byte block,
+    # 1,153 of them 8-byte encodings: per G function 6 v_lshl_add_u64 (64-bit
+    # adds), 6 v_alignbit_b32 (rotations by 24, 16, 63; by 32 is a swap) and 8
+    # v_xor_b32; 96 G per block.  Each kernel below holds one compression body
+    # (k_hash_leaves<true> two: whole leaves and the word-by-word tail).
+    ks, _ = kernels
+    bodies = {"k_adamw_hash_leaves": 1, "k_hash_level": 1, "k_hash_tail": 1}
+    seen = set()
+    for name, ops in ks.items():
+        s = _short(name)
+        k = bodies.get(s, 2 if "hash_leavesILb1" in name else 1 if s == "k_hash_leaves" else 0)
+        if not k:
+            continue
+        assert ops["v_alignbit_b32"] == 576 * k, (s, ops["v_alignbit_b32"])
+        assert 576 * k <= ops["v_lshl_add_u64"] <= 576 * k + 16, (s, ops["v_lshl_add_u64"])
+        assert 784 * k <= ops["v_xor_b32_e32"] <= (784 + 30) * k, (s, ops["v_xor_b32_e32"])
+        seen.add(name)
+    assert len(seen) == 5
