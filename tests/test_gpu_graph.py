@@ -116,3 +116,41 @@ def test_captured_step_replays_bit_for_bit():
     assert_bitwise(got["m"], mr, "bf16 m")
     assert_bitwise(got["v"], vr, "bf16 v")
     assert br.read_step_state(captured.bstate)["step"] == 4
+
+
+def test_captured_no_allocation_update_and_hash():
+    # The no-allocation AdamW + state hash is for callers that capture: its
+    # digests live in the library's own array, so the captured graph holds
+    # only kernels.  Three replays (each one more AdamW step at t = 7 on the
+    # same state), each against the workspace form called eagerly on a copy.
+    n = 1024 * 40
+    st0 = np.concatenate([synth.generate(n, synth.NORMAL, synth.tid(8, 0x20), 0.02),
+                          synth.generate(n, synth.NORMAL, synth.tid(8, 0x21), 1e-4),
+                          np.abs(synth.generate(n, synth.NORMAL, synth.tid(8, 0x22), 1e-6))])
+    g = synth.generate(n, synth.NORMAL, synth.tid(8, 0x23), 1e-3)
+    hp = dict(lr=3e-4, beta1=0.9, beta2=0.999, eps=1e-8, weight_decay=0.1, step=7)
+    dg = to_dev(g)
+    cap_state, eager_state, warm_state = to_dev(st0), to_dev(st0), to_dev(st0)
+    cap_digest = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    eager_digest = torch.zeros(32, dtype=torch.uint8, device="cuda")
+    ws = br.hash_workspace(3 * n)
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):  # first call (and the array's address lookup) outside the capture
+        br.repro_adamw_hash_noalloc(warm_state, dg, torch.empty_like(cap_digest), **hp)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        br.repro_adamw_hash_noalloc(cap_state, dg, cap_digest, **hp)
+    torch.cuda.synchronize()
+    ref = st0.copy()
+    for k in range(3):
+        graph.replay()
+        br.repro_adamw_hash(eager_state, dg, eager_digest, ws, **hp)
+        torch.cuda.synchronize()
+        assert torch.equal(cap_state.view(torch.int32), eager_state.view(torch.int32)), f"replay {k}: state"
+        assert torch.equal(cap_digest, eager_digest), f"replay {k}: digest"
+        oracle.adamw_inplace(ref, g, **hp)
+    assert_bitwise(to_host(cap_state), ref, "state after three replays")
+    assert bytes(to_host(cap_digest).tobytes()) == oracle.state_hash(ref)
