@@ -257,6 +257,9 @@ hipError_t side_stream(int device, size_t nevents, SideStream** out) {
 }
 
 constexpr int64_t kLeafWords = 1024;            // a 4096-byte hash leaf
+// The largest word count the hash accepts: its byte count, and every level's
+// digest bytes, stay far inside int64 (2^60 words = 4 EiB).
+constexpr int64_t kMaxHashWords = int64_t(1) << 60;
 // Pipelined form: 2^26 elements per chunk, 196,608 leaves per hash launch
 // (768 workgroups), the fastest of 2^23 .. 2^28 measured on the optimizer
 // workload.
@@ -268,6 +271,7 @@ int repro_adamw_hash(float* state, const float* grad, int64_t n, float lr, float
                      float weight_decay, int64_t step, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
                      int64_t chunk, void* stream) {
   if (n < 0 || step < 1 || workspace == nullptr || digest_out == nullptr) return REPRO_EINVAL;
+  if (n > kMaxHashWords / 3) return REPRO_EINVAL;
   if (chunk > 0 && chunk % kLeafWords != 0) return REPRO_EINVAL;
   if (n > 0 && (state == nullptr || grad == nullptr)) return REPRO_EINVAL;
   if (n > 0 && (!aligned4(state) || !aligned4(grad))) return REPRO_EALIGN;
@@ -390,7 +394,7 @@ int repro_adamw_hash_noalloc(float* state, const float* grad, int64_t n, float l
 }
 
 int64_t repro_state_hash_workspace_bytes(int64_t n_words) {
-  if (n_words < 0) return REPRO_EINVAL;
+  if (n_words < 0 || n_words > kMaxHashWords) return REPRO_EINVAL;
   repro::HashPlan plan;
   repro::plan_state_hash(n_words, &plan);
   return plan.total_bytes;
@@ -398,7 +402,7 @@ int64_t repro_state_hash_workspace_bytes(int64_t n_words) {
 
 int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64_t ws_bytes, uint8_t* digest_out,
                      void* stream) {
-  if (n_words < 0 || workspace == nullptr || digest_out == nullptr) return REPRO_EINVAL;
+  if (n_words < 0 || n_words > kMaxHashWords || workspace == nullptr || digest_out == nullptr) return REPRO_EINVAL;
   if (n_words > 0 && words == nullptr) return REPRO_EINVAL;
   if (n_words > 0 && !aligned4(words)) return REPRO_EALIGN;
   if ((reinterpret_cast<uintptr_t>(workspace) & 15u) != 0 || (reinterpret_cast<uintptr_t>(digest_out) & 15u) != 0)

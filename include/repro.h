@@ -319,7 +319,9 @@ int repro_adamw_bf16_step(uint16_t* w, float* m, float* v, const void* grad, int
  * The root digest is the state hash.  Hash [w | m | v] by passing
  * state and 3n.
  *
- *   words:      device pointer to n_words floats (n_words >= 0).
+ *   words:      device pointer to n_words floats (0 <= n_words <= 2^60;
+ *               larger counts return REPRO_EINVAL, as does
+ *               repro_state_hash_workspace_bytes for them).
  *   workspace:  device memory of at least
  *               repro_state_hash_workspace_bytes(n_words) bytes, 16-byte
  *               aligned, used for the digests of every level.
@@ -350,7 +352,7 @@ int repro_state_hash(const float* words, int64_t n_words, void* workspace, int64
  *          the two run in turn);
  *   chunk < 0: the update, then the hash, both on the caller's stream.
  *
- *   state, grad, n, lr ... step: as repro_adamw.
+ *   state, grad, n, lr ... step: as repro_adamw (n <= 2^60 / 3).
  *   workspace, ws_bytes: as repro_state_hash for 3n words.
  *   digest_out: device pointer to 32 bytes (16-byte aligned).
  * Asynchronous: the caller's stream is ordered after all of the work.  For

@@ -52,6 +52,10 @@ def test_host_side_argument_checks():
     assert lib.repro_fp32_ops(7, 16, 16, 16, 4, null) == -1
     assert lib.repro_state_hash(16, -1, 16, 1 << 20, 16, null) == -1
     assert lib.repro_state_hash(16, 1024, 16, 0, 16, null) == -4  # workspace too small
+    # Word counts whose byte count would leave int64 are refused, not wrapped.
+    assert lib.repro_state_hash(16, 2**62, 16, 2**40, 16, null) == -1
+    assert br.library().repro_state_hash_workspace_bytes(2**62) == -1
+    assert lib.repro_adamw_hash(16, 16, 2**61, 1e-3, 0.9, 0.999, 1e-8, 0.1, 1, 16, 2**40, 16, 0, null) == -1
     # Replay: buffer counts whose product would wrap int64 (64 * 2^31-1 * 2^31-1)
     # or exceed the buffer limit are refused before the pointer array is read.
     big = 2**31 - 1
