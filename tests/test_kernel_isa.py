@@ -85,7 +85,7 @@ def test_fused_kernels_use_the_declared_units(kernels):
             assert ops["v_add_f32_e32"] == 0 and ops["v_add_f32_e64"] == 0
             assert not any(FUSED_OR_PACKED.match(op) for op in ops)
         elif s == "k_gemm_fma":
-            assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 1024
+            assert ops["v_fmac_f32_e32"] + ops["v_fma_f32"] >= 2048  # 32 k steps x 8 x 8 outputs per lane
             assert ops["v_add_f32_e32"] == 0
         elif s == "k_fma_mfma":
             # One K = 1 matrix instruction per instantiation (32x32, 16x16 or 4x4 blocks).
