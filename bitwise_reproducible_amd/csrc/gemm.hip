@@ -241,10 +241,10 @@ __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm_fma(
 // blocks, D = C + a_i * b_j with one rounding.  With C = -0 (the additive
 // identity of IEEE addition, which keeps the sign of a zero product) every D
 // element is exactly fl(a_i * b_j) under the contract, including the flush
-// rule and signed zeros; this was checked bit for bit against v_mul_f32 on
-// ~10^8 products (random exponents, exact ties, products at +-2^-126,
-// zero and subnormal operands, overflow), and the GEMM parity tests check the
-// result.  No sum is formed inside the matrix core: each product then takes
+// rule and signed zeros.  The tests check the single step with C = -0
+// against the oracle's multiply (products within ulps of +-2^-126, exact
+// ties, subnormal operands, overflow, signed zeros), and run this variant's
+// GEMM on the same kinds of data.  No sum is formed inside the matrix core: each product then takes
 // its place in the output's own chain with a v_add_f32, k ascending, so the
 // declared order is unchanged while the multiplies leave the VALU.
 //
