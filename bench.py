@@ -12,8 +12,9 @@ every input already resident in HBM:
   4. repro_gemm          dW[2048x8192] = X^T dY, X[16384x2048], dY[16384x8192]
 Each op is bracketed by HIP events on the stream it runs on.  `value` is the
 GB/s of the memory-side work (reduce bytes, AdamW bytes and the hashed bytes
-over the event time of ops 1 and 3); the GEMMs are reported in GFLOP/s
-beside it.  After the steps, and not part of them: repro_adamw and
+over the event time of ops 1 and 3; the hashed bytes are read from LDS, not
+HBM, so `hbm_gbps` gives the rate of the bytes that cross HBM); the GEMMs
+are reported in GFLOP/s beside it.  After the steps, and not part of them: repro_adamw and
 repro_state_hash as separate calls ("ops_in_turn", each kernel's own
 roofline), and under "next_rows" the audit replay of one step's reduction
 (OPEN-1B section 6, Algorithm 1: 6 replicas x 8 shards x 6 microbatches over
@@ -25,7 +26,7 @@ columns of the GEMMs, sampled AdamW elements replayed through every step,
 sampled hash leaves, the replay and BF16 step on samples), and the oracle
 itself is timed on a bounded sample as the CPU baseline.
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--gemm-variants]
 """
 import argparse
 import json
