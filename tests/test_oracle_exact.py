@@ -165,3 +165,79 @@ def test_adamw_element_sequence(step):
     got = oracle.adamw(np.concatenate([w, m, v]), g, **hp)
     wn, mn, vn = _adamw_exact(w, m, v, g, 3e-4, 0.9, 0.999, 1e-8, 0.1, step)
     assert np.array_equal(_words(got), _words(np.concatenate([wn, mn, vn])))
+
+
+@pytest.mark.parametrize("layout", [(2, 3, 2), (3, 2, 1), (1, 1, 4), (5, 1, 1), (1, 4, 3)])
+def test_replay_reduce(layout):
+    # Algorithm 1 (section 6) with Appendix A.1-A.3, written on exact operations:
+    # microbatch terms scaled before they are added, shards summed in ascending
+    # order from a copy of shard 0, each replica's sum scaled and pushed into
+    # TreeFold, the result scaled by the replica reciprocal.
+    rep_n, shard_n, accum = layout
+    rng = np.random.default_rng(sum(layout) * 7 + accum)
+    n = 12
+    grads = [_f32(rng.standard_normal(n) * 10.0 ** rng.integers(-3, 3, n)) for _ in range(rep_n * shard_n * accum)]
+    one = np.float32(1.0)
+    ra, rs, rr = (X.div(one, np.float32(d)) for d in (accum, shard_n, rep_n))
+    want = np.empty(n, np.float32)
+    for i in range(n):
+        parts = []
+        for rep in range(rep_n):
+            inner = None
+            for shard in range(shard_n):
+                r = rep * shard_n + shard
+                g = np.float32(0.0)
+                for k in range(accum):
+                    g = X.add(g, X.mul(grads[r * accum + k][i], ra))
+                inner = g if shard == 0 else X.add(inner, g)
+            parts.append(X.mul(inner, rs))
+        want[i] = X.mul(_treefold(parts), rr)
+    assert np.array_equal(_words(oracle.replay_reduce(grads, *layout)), _words(want))
+
+
+def _bf16_round_exact(x):
+    """binary32 -> bf16 pattern: the exact value rounded to 8 significant bits,
+    nearest-even; past the largest bf16, an infinity."""
+    s, m = X.decode(x)
+    if m == 0:
+        return np.uint16(s << 15)
+    e = m.numerator.bit_length() - m.denominator.bit_length()
+    if X.Fraction(2) ** e > m:
+        e -= 1
+    q = m / X.Fraction(2) ** (e - 7)
+    k = q.numerator // q.denominator
+    rem = q - k
+    if rem > X.Fraction(1, 2) or (rem == X.Fraction(1, 2) and k % 2 == 1):
+        k += 1
+    if k == 256:
+        k, e = 128, e + 1
+    if e > 127:
+        return np.uint16((s << 15) | 0x7F80)
+    return np.uint16((s << 15) | ((e + 127) << 7) | (k & 0x7F))
+
+
+def test_bf16_rounding_and_one_clipped_step():
+    rng = np.random.default_rng(77)
+    n = 96
+    x = _f32(rng.uniform(1, 2, 400) * 2.0 ** rng.integers(-120, 127, 400) * rng.choice([-1, 1], 400))
+    x[:4] = _f32([3.3895314e38, -3.3961776e38, 1.0 + 2.0 ** -8, 1.0 + 3 * 2.0 ** -8])  # overflow and both tie parities
+    assert np.array_equal(oracle.bf16_round(x), np.array([_bf16_round_exact(v) for v in x], np.uint16))
+    # One BF16 step from m = v = 0 with a gradient whose norm (~3) is clipped to 1.
+    w16 = oracle.bf16_round(_f32(rng.standard_normal(n) * 0.02))
+    g16 = oracle.bf16_round(_f32(rng.standard_normal(n) * 0.3))
+    m = np.zeros(n, np.float32)
+    v = np.zeros(n, np.float32)
+    gw = oracle.bf16_widen(g16)
+    S = _treefold([X.mul(gi, gi) for gi in gw])
+    norm = X.sqrt(S)
+    assert oracle.grad_norm(g16, return_sumsq=True) == (norm, S)
+    coef = X.div(np.float32(1.0), X.add(norm, np.float32(1e-6)))
+    assert coef < 1
+    gc = np.array([X.mul(gi, coef) for gi in gw], np.float32)
+    wn, mn, vn = _adamw_exact(oracle.bf16_widen(w16), m, v, gc, 3e-4, 0.9, 0.95, 1e-8, 0.1, 1)
+    st = oracle.new_step_state()
+    wo, mo, vo = w16.copy(), m.copy(), v.copy()
+    oracle.adamw_bf16_step(wo, mo, vo, g16, st, lr=3e-4, beta1=0.9, beta2=0.95, eps=1e-8, weight_decay=0.1,
+                           max_norm=1.0, spike_threshold=5.0, skip_steps=5)
+    assert np.array_equal(wo, np.array([_bf16_round_exact(x) for x in wn], np.uint16))
+    assert np.array_equal(_words(mo), _words(mn)) and np.array_equal(_words(vo), _words(vn))
