@@ -30,6 +30,8 @@
 //    reads a and b fragments as 16-byte LDS vectors.
 #include <hip/hip_runtime.h>
 
+#include <type_traits>
+
 #include "internal.h"
 
 namespace repro {
@@ -69,10 +71,12 @@ __device__ __forceinline__ float4 load_chunk(const float* __restrict__ p, int64_
   return v;
 }
 
+typedef float v4f __attribute__((ext_vector_type(4)));
+
 template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC, bool FUSED>
 __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
                                           int64_t lda, const float* __restrict__ B, int64_t ldb,
-                                          float* __restrict__ C, int64_t ldc, int tiles_n) {
+                                          float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
   using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
   __shared__ __attribute__((aligned(16))) float As[2][BK][BM + T::PAD];
   __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + T::PAD];
@@ -84,36 +88,71 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
   const int tx = tid % T::TX;
   const int ty = tid / T::TX;
 
-  float4 ra[T::LA], rb[T::LB];
+  v4f ra[T::LA], rb[T::LB];
 
-  // Global -> registers for the slab starting at k0.
-  auto load_slab = [&](int64_t k0) {
+  // Global -> registers for the slab starting at k0, bounds-checked.
+  auto load_slab = [&](int64_t k0) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T::LA; ++q) {
       const int f = tid + q * T::NT;
+      float4 v;
       if constexpr (!TA) {  // A is M x K row-major: rows i, contiguous k
         const int r = f / (BK / 4), c4 = f % (BK / 4);
-        ra[q] = load_chunk<VEC>(A, i0 + r, k0 + 4 * c4, lda, M, K);
+        v = load_chunk<VEC>(A, i0 + r, k0 + 4 * c4, lda, M, K);
       } else {  // A stored K x M: rows k, contiguous i
         const int c = f / (BM / 4), r4 = f % (BM / 4);
-        ra[q] = load_chunk<VEC>(A, k0 + c, i0 + 4 * r4, lda, K, M);
+        v = load_chunk<VEC>(A, k0 + c, i0 + 4 * r4, lda, K, M);
       }
+      ra[q] = v4f{v.x, v.y, v.z, v.w};
     }
 #pragma unroll
     for (int q = 0; q < T::LB; ++q) {
       const int f = tid + q * T::NT;
+      float4 v;
       if constexpr (!TB) {  // B is K x N row-major: rows k, contiguous j
         const int c = f / (BN / 4), j4 = f % (BN / 4);
-        rb[q] = load_chunk<VEC>(B, k0 + c, j0 + 4 * j4, ldb, K, N);
+        v = load_chunk<VEC>(B, k0 + c, j0 + 4 * j4, ldb, K, N);
       } else {  // B stored N x K: rows j, contiguous k
         const int j = f / (BK / 4), c4 = f % (BK / 4);
-        rb[q] = load_chunk<VEC>(B, j0 + j, k0 + 4 * c4, ldb, N, K);
+        v = load_chunk<VEC>(B, j0 + j, k0 + 4 * c4, ldb, N, K);
       }
+      rb[q] = v4f{v.x, v.y, v.z, v.w};
     }
   };
 
+  // Interior tiles (the whole BM x BN tile inside C, 16-byte rows, and every
+  // lane's offset inside a slab below 2^32 bytes): each lane's offsets are
+  // formed once, the slab base advances as a wave-uniform 64-bit address,
+  // and the loads carry no bounds checks.
+  const bool interior = VEC && off32 && i0 + BM <= M && j0 + BN <= N;
+  uint32_t oa[T::LA], ob[T::LB];
+#pragma unroll
+  for (int q = 0; q < T::LA; ++q) {
+    const int f = tid + q * T::NT;
+    oa[q] = !TA ? (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * lda + 4 * (f % (BK / 4))))
+                : (uint32_t)(4 * ((int64_t)(f / (BM / 4)) * lda + 4 * (f % (BM / 4))));
+  }
+#pragma unroll
+  for (int q = 0; q < T::LB; ++q) {
+    const int f = tid + q * T::NT;
+    ob[q] = !TB ? (uint32_t)(4 * ((int64_t)(f / (BN / 4)) * ldb + 4 * (f % (BN / 4))))
+                : (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * ldb + 4 * (f % (BK / 4))));
+  }
+  const char* const abase = reinterpret_cast<const char*>(TA ? A + i0 : A + i0 * lda);
+  const char* const bbase = reinterpret_cast<const char*>(TB ? B + j0 * ldb : B + j0);
+  const int64_t astep = 4 * (TA ? BK * lda : BK);
+  const int64_t bstep = 4 * (TB ? BK : BK * ldb);
+  auto load_slab_interior = [&](int64_t s) __attribute__((always_inline)) {
+    const char* ab = abase + s * astep;
+    const char* bb = bbase + s * bstep;
+#pragma unroll
+    for (int q = 0; q < T::LA; ++q) ra[q] = *reinterpret_cast<const v4f*>(ab + oa[q]);
+#pragma unroll
+    for (int q = 0; q < T::LB; ++q) rb[q] = *reinterpret_cast<const v4f*>(bb + ob[q]);
+  };
+
   // Registers -> LDS, k-major.
-  auto store_slab = [&](int buf) {
+  auto store_slab = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
     for (int q = 0; q < T::LA; ++q) {
       const int f = tid + q * T::NT;
@@ -125,7 +164,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
         As[buf][4 * c4 + 3][r] = ra[q].w;
       } else {
         const int c = f / (BM / 4), r4 = f % (BM / 4);
-        *reinterpret_cast<float4*>(&As[buf][c][4 * r4]) = ra[q];
+        *reinterpret_cast<v4f*>(&As[buf][c][4 * r4]) = ra[q];
       }
     }
 #pragma unroll
@@ -133,7 +172,7 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
       const int f = tid + q * T::NT;
       if constexpr (!TB) {
         const int c = f / (BN / 4), j4 = f % (BN / 4);
-        *reinterpret_cast<float4*>(&Bs[buf][c][4 * j4]) = rb[q];
+        *reinterpret_cast<v4f*>(&Bs[buf][c][4 * j4]) = rb[q];
       } else {
         const int j = f / (BK / 4), c4 = f % (BK / 4);
         Bs[buf][4 * c4 + 0][j] = rb[q].x;
@@ -150,49 +189,91 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
 #pragma unroll
     for (int j = 0; j < TN; ++j) acc[i][j] = 0.0f;  // the chain starts at +0
 
-  // One k step: every output of the lane takes fl(acc + fl(a * b)), or
-  // fl(a * b + acc) rounded once under the fused convention.
-  auto mac_step = [&](int buf, int kk) {
-    float a[TM], b[TN];
+  // Register fragments of one k step: the lane's TM values of A and TN of B.
+  float fa[2][TM], fb[2][TN];
+  auto read_frag = [&](int slot, int buf, int kk) __attribute__((always_inline)) {
 #pragma unroll
     for (int g = 0; g < TM / 4; ++g)
-      *reinterpret_cast<float4*>(&a[4 * g]) =
-          *reinterpret_cast<const float4*>(&As[buf][kk][g * 4 * T::TY + ty * 4]);
+      *reinterpret_cast<v4f*>(&fa[slot][4 * g]) =
+          *reinterpret_cast<const v4f*>(&As[buf][kk][g * 4 * T::TY + ty * 4]);
 #pragma unroll
     for (int g = 0; g < TN / 4; ++g)
-      *reinterpret_cast<float4*>(&b[4 * g]) =
-          *reinterpret_cast<const float4*>(&Bs[buf][kk][g * 4 * T::TX + tx * 4]);
+      *reinterpret_cast<v4f*>(&fb[slot][4 * g]) =
+          *reinterpret_cast<const v4f*>(&Bs[buf][kk][g * 4 * T::TX + tx * 4]);
+  };
+  // One k step: every output of the lane takes fl(acc + fl(a * b)), or
+  // fl(a * b + acc) rounded once under the fused convention.
+  auto mac_frag = [&](int slot) __attribute__((always_inline)) {
 #pragma unroll
     for (int i = 0; i < TM; ++i)
 #pragma unroll
       for (int j = 0; j < TN; ++j) {
         if constexpr (FUSED) {
-          acc[i][j] = __builtin_fmaf(a[i], b[j], acc[i][j]);
+          acc[i][j] = __builtin_fmaf(fa[slot][i], fb[slot][j], acc[i][j]);
         } else {
-          const float p = a[i] * b[j];
+          const float p = fa[slot][i] * fb[slot][j];
           acc[i][j] = acc[i][j] + p;
         }
       }
   };
+  // A full slab, k ascending.  The LDS reads of step kk + 1 are issued
+  // before the multiplies of step kk (the scheduling barriers keep the
+  // compiler from sinking them to their use), so a wave does not wait on LDS
+  // latency between steps; this only moves loads, never the order of a chain.
+  auto full_slab = [&](int buf) __attribute__((always_inline)) {
+    read_frag(0, buf, 0);
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      if (kk + 1 < BK) read_frag((kk + 1) & 1, buf, kk + 1);
+      __builtin_amdgcn_sched_barrier(0);
+      mac_frag(kk & 1);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
 
+  // Slabs 0 .. nfull-1 are full; a last, partial one holds K - nfull * BK
+  // steps.  Interior tiles (which need K to be a whole number of slabs) and
+  // the others run separate copies of the slab loop: the same steps in the
+  // same order, other loads.
+  const int64_t nfull = K / BK;
   const int64_t nslabs = (K + BK - 1) / BK;
-  if (nslabs > 0) {
-    load_slab(0);
+  auto run = [&](auto interior_tag) __attribute__((always_inline)) {
+    constexpr bool kInterior = decltype(interior_tag)::value;
+    if constexpr (kInterior) {
+      load_slab_interior(0);
+    } else {
+      load_slab(0);
+    }
     store_slab(0);
     __syncthreads();
-    for (int64_t s = 0; s < nslabs; ++s) {
-      const int buf = (int)(s & 1);
-      if (s + 1 < nslabs) load_slab((s + 1) * BK);
-      const int64_t kleft = K - s * BK;
-      if (kleft >= BK) {
-#pragma unroll
-        for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
+    int buf = 0;
+    // The loop body is the same on every pass (a conditional prefetch makes
+    // the compiler spill): an interior tile reloads its last slab on the
+    // last pass, the bounds-checked loads read past K as zeros.  Either way
+    // the extra slab lands in the buffer that is no longer read.
+    for (int64_t s = 0; s < nfull; ++s) {
+      if constexpr (kInterior) {
+        load_slab_interior(s + 1 < nfull ? s + 1 : s);
       } else {
-        for (int kk = 0; kk < (int)kleft; ++kk) mac_step(buf, kk);
+        load_slab((s + 1) * BK);
       }
-      if (s + 1 < nslabs) store_slab(buf ^ 1);
+      full_slab(buf);
+      store_slab(buf ^ 1);
       __syncthreads();
+      buf ^= 1;
     }
+    if constexpr (!kInterior) {
+      const int kleft = (int)(K - nfull * BK);
+      for (int kk = 0; kk < kleft; ++kk) {
+        read_frag(0, buf, kk);
+        mac_frag(0);
+      }
+    }
+  };
+  if (interior && K % BK == 0 && nfull > 0) {
+    run(std::true_type{});
+  } else if (nslabs > 0) {
+    run(std::false_type{});
   }
 
   // Epilogue: lane rows g*4*TY + ty*4 + e, columns h*4*TX + tx*4 + 0..3.
@@ -222,16 +303,16 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
 template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
-    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
-  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
+  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n, off32);
 }
 
 // The fused convention on the VALU: one v_fma_f32 per step of each chain.
 template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__((BM / TM) * (BN / TN)) void k_gemm_fma(
     int64_t M, int64_t N, int64_t K, const float* __restrict__ A, int64_t lda, const float* __restrict__ B,
-    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n) {
-  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+    int64_t ldb, float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
+  gemm_tile<BM, BN, BK, TM, TN, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n, off32);
 }
 
 // ---------------------------------------------------------------------------
@@ -454,12 +535,18 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  // Largest byte offset of a lane inside one slab, from the slab's base:
+  // interior tiles address slabs with 32-bit lane offsets when it fits.
+  const int64_t a_span = TA ? (int64_t)BK * lda + BM : (int64_t)BM * lda + BK;
+  const int64_t b_span = TB ? (int64_t)BN * ldb + BK : (int64_t)BK * ldb + BN;
+  const int off32 = (lda < ((int64_t)1 << 40) && ldb < ((int64_t)1 << 40) && 4 * a_span < ((int64_t)1 << 32) &&
+                     4 * b_span < ((int64_t)1 << 32)) ? 1 : 0;
   if constexpr (FUSED)
     hipLaunchKernelGGL((k_gemm_fma<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0,
-                       stream, M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
+                       stream, M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n, off32);
   else
     hipLaunchKernelGGL((k_gemm<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0, stream,
-                       M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n);
+                       M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n, off32);
   return hipGetLastError();
 }
 
