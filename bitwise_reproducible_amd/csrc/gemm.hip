@@ -591,10 +591,18 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   if (variant == 2)
     return dispatch<64, 64, 16, 4, 4, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   if (variant == 3) return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  // 32-deep k slabs: half the barriers and slab loads per MAC of 16-deep
-  // ones; measured on MI355X 2% faster on the weight-gradient workload and
-  // 1-10% on the forward one, same bits (213 and 249 VGPRs: still two waves
-  // per SIMD; 67.6 KB of LDS: two workgroups per CU).
+  // Large outputs: 256 x 128 tiles, 16 x 8 outputs per lane, 16-deep slabs
+  // (250 VGPRs: two waves per SIMD; 50 KB of LDS).  Each k step reads 24
+  // values from LDS for 128 MACs instead of 16 for 64, and each slab moves
+  // half as many A and B bytes per MAC; measured on MI355X 3-4% faster than
+  // 128 x 128 tiles on both GEMM workloads, same bits.  Used when there are
+  // at least two such tiles per CU, so the larger tile costs no parallelism.
+  if (variant == 0 && ((M + 255) / 256) * ((N + 127) / 128) >= 512)
+    return dispatch<256, 128, 16, 16, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
+  // Otherwise 128 x 128 tiles with 32-deep k slabs: half the barriers and
+  // slab loads per MAC of 16-deep ones; measured on MI355X 2% faster on the
+  // weight-gradient workload and 1-10% on the forward one, same bits (two
+  // waves per SIMD; 67.6 KB of LDS: two workgroups per CU).
   return dispatch<128, 128, 32, 8, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 

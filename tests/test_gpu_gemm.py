@@ -55,6 +55,25 @@ def test_many_tiles_with_ragged_edges(ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
 
+@pytest.mark.parametrize("K", [80, 77])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_large_output_tiles_every_word(ta, tb, K):
+    # 4173 x 4141 outputs: 17 x 33 = 561 tiles of 256 x 128, enough for the
+    # default variant to take its large-output kernel, with partial tiles in
+    # M and N.  K = 80 is five whole 16-deep slabs (interior tiles take the
+    # unchecked loads), K = 77 ends in a partial slab (every tile checked).
+    # Every output word against the oracle, and against the 128 x 128 kernel
+    # of variant 1.
+    M, N = 4173, 4141
+    A, B = _stored(M, N, K, ta, tb, 0x8900 + 4 * ta + 2 * tb + (K & 1))
+    ref = oracle.gemm(A, B, bool(ta), bool(tb))
+    dA, dB = to_dev(A), to_dev(B)
+    C0 = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=0)
+    assert_bitwise(to_host(C0), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant=0")
+    C1 = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=1)
+    assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
+
+
 def test_tiny_workload():
     a, b = synth.tiny_gemm_inputs()
     C = br.repro_gemm(to_dev(a), to_dev(b))

@@ -110,6 +110,13 @@ def test_unfused_gemm_chain_is_one_multiply_and_one_add_per_step(kernels):
             assert ops["v_mul_f32_e32"] >= 2048 and ops["v_add_f32_e32"] >= 2048, ops
             seen += 1
     assert seen == 8  # the default kernel, 4 transposes x 2 load widths
+    seen = 0
+    for name, ops in ks.items():
+        if _short(name) == "k_gemm" and "Li256ELi128ELi16ELi16ELi8E" in name:
+            # The large-output kernel: 16 k steps x 16 x 8 outputs per lane.
+            assert ops["v_mul_f32_e32"] >= 2048 and ops["v_add_f32_e32"] >= 2048, ops
+            seen += 1
+    assert seen == 8
 
 
 def test_no_kernel_uses_scratch(kernels):
