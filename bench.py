@@ -26,7 +26,7 @@ columns of the GEMMs, sampled AdamW elements replayed through every step,
 sampled hash leaves, the replay and BF16 step on samples), and the oracle
 itself is timed on a bounded sample as the CPU baseline.
 
-Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--gemm-variants]
+Usage: python bench.py [--gpus 1] [--steps 10] [--warmup 3] [--gemm-variants | --valu-rates]
 """
 import argparse
 import json
@@ -42,33 +42,37 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, vendor figure
 FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
 # VALU issue rate: 256 CUs x 128 fp32 lanes per clock x 2.4 GHz = 78.6 T
 # lane-operations/s (the vendor fp32 figure is this rate times 2 flops per
-# FMA).  The declared MAC is a multiply and an add, two lane-ops for two
-# flops, so the GEMM's ceiling is 78.6 TFLOP/s.  32-bit integer ops issue at
-# the same rate (measured), which bounds the hash.
+# FMA), i.e. 0.5 wave-instructions per SIMD per clock.  The declared MAC is a
+# multiply and an add, two lane-ops for two flops, so the GEMM's ceiling is
+# 78.6 TFLOP/s.  Full-rate opcodes (v_mul_f32, v_add_f32, v_xor_b32,
+# v_lshrrev_b32, ...) reach it in either encoding; `bench.py --valu-rates`
+# measures 0.47-0.48 for long streams of them.
 VALU_LANE_OPS = 256 * 128 * 2.4e9
 GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
 # BLAKE2b: per 128-byte block 12 rounds x 8 G.  The compiled compression
 # (k_hash_leaves, gfx950) is 2001 VALU instructions: 802 v_xor_b32 and 46
-# other 4-byte ones, 577 v_lshl_add_u64 (one per 64-bit add) and 576
+# other full-rate ones, 577 v_lshl_add_u64 (one per 64-bit add) and 576
 # v_alignbit_b32 (two per rotation by 24, 16 or 63); the rotation by 32 is a
 # register swap.  The instruction audit in the tests checks these counts.
 HASH_VALU_PER_BLOCK = 2001
-HASH_VALU_8BYTE_PER_BLOCK = 1153   # v_lshl_add_u64 + v_alignbit_b32: 8-byte (VOP3) encodings
+HASH_VALU_HALF_RATE_PER_BLOCK = 1153   # v_lshl_add_u64 + v_alignbit_b32
 # Bound 1 (the `peak` of the hash rows): one issue slot per VALU instruction
 # at the VALU issue rate above.
 HASH_INSTR_PER_BYTE = HASH_VALU_PER_BLOCK / 128
 HASH_PEAK_GBS = VALU_LANE_OPS / HASH_INSTR_PER_BYTE / 1e9
-# Bound 2 (reported beside it as `*_issue_model`): an 8-byte encoding takes
-# two issue slots.  This is an assumption about gfx950's issue, supported by
-# the kernels' own counters: the unfused GEMM (4-byte VALU instructions only)
-# issues 0.39-0.42 wave-instructions per SIMD per clock and the leaf hash
-# (58% 8-byte) 0.255, which that rule predicts (0.27).
-HASH_SLOTS_PER_BYTE = (HASH_VALU_PER_BLOCK + HASH_VALU_8BYTE_PER_BLOCK) / 128
+# Bound 2 (reported beside it as `*_issue_model`), from `bench.py
+# --valu-rates`: v_alignbit_b32 and v_lshl_add_u64 are half-rate opcodes
+# (0.22-0.24 wave-instructions per SIMD per clock alone), and a stream that
+# interleaves them with full-rate ones, as every G function does, issues all
+# of its instructions at that half rate (0.23-0.24 for alternating
+# v_alignbit_b32 / v_xor_b32; only a long full-rate run amortises a short
+# cluster of half-rate ones).  So each hash instruction takes two slots.
+HASH_SLOTS_PER_BYTE = 2 * HASH_INSTR_PER_BYTE
 HASH_MODEL_PEAK_GBS = VALU_LANE_OPS / HASH_SLOTS_PER_BYTE / 1e9
 # The AdamW update in the fused kernel: 190 VALU instructions per four
 # elements (16 operations each, with the correctly rounded division and
-# square-root sequences), 47.5 per element, all 4-byte encodings but the
-# division's v_div_scale / v_div_fmas / v_div_fixup and a few fma.
+# square-root sequences), 47.5 per element.  The issue model counts them at
+# the half rate too: the fused kernel's waves interleave them with the hash.
 ADAMW_INSTR_PER_ELEMENT = 47.5
 
 
@@ -113,6 +117,10 @@ def parse():
                    help="only the forward GEMM workload, once each with repro_gemm variant 0 (VALU), variant 3 "
                         "(matrix-core products, VALU adds) and repro_gemm_fma variant 0 (matrix cores), after one "
                         "warm-up each: the run the matrix-core co-execution counters are taken on")
+    p.add_argument("--valu-rates", action="store_true",
+                   help="only the VALU issue-rate streams of libvalu_rates.so (single-opcode streams and the "
+                        "interleavings of full- and half-rate opcodes that the kernels contain): the measurement "
+                        "behind the ALU bounds")
     p.add_argument("--calibration-copy", action="store_true",
                    help="after timing, run one plain copy of 64 MiB (a one-replica fold without the average) whose "
                         "HBM counters calibrate the FETCH_SIZE / WRITE_SIZE readings of a profiling run")
@@ -159,6 +167,9 @@ def main():
     torch.cuda.set_device(dev)
     if args.gemm_variants:
         gemm_variants(torch, np, br, synth, dev)
+        return
+    if args.valu_rates:
+        valu_rates()
         return
     up = Upload(torch)
     t_setup = time.time()
@@ -403,7 +414,7 @@ def main():
             # issue of the hash plus the update (instructions per element).
             t_hbm = bytes_adamw / (HBM_PEAK_GBS * 1e9)
             t_alu = n * (12 * HASH_INSTR_PER_BYTE + ADAMW_INSTR_PER_ELEMENT) / VALU_LANE_OPS
-            t_model = n * (12 * HASH_SLOTS_PER_BYTE + ADAMW_INSTR_PER_ELEMENT) / VALU_LANE_OPS
+            t_model = n * (12 * HASH_SLOTS_PER_BYTE + 2 * ADAMW_INSTR_PER_ELEMENT) / VALU_LANE_OPS
             t_bound = max(t_hbm, t_alu)
             peak = bytes_hash / t_bound / 1e9
             ach = bytes_hash / (ms * 1e-3) / 1e9
@@ -492,6 +503,31 @@ def main():
     if not args.no_cpu_baseline:
         out["cpu_baseline"] = cpu_baseline(np)
     print(json.dumps(out), flush=True)
+
+
+def valu_rates():
+    """Wave-instructions per SIMD per shader clock of the streams in
+    libvalu_rates.so, with 2 and 4 waves on every SIMD."""
+    import ctypes
+    path = os.path.join(ROOT, "bitwise_reproducible_amd", "libvalu_rates.so")
+    if not os.path.exists(path):
+        raise RuntimeError(f"{path} is not built: run __graft_entry__.build() first")
+    lib = ctypes.CDLL(path)
+    lib.valu_rates_name.restype = ctypes.c_char_p
+    lib.valu_rates_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    out = []
+    for s in range(lib.valu_rates_count()):
+        name = lib.valu_rates_name(s).decode()
+        row = {"stream": name}
+        for w in (2, 4):
+            res = (ctypes.c_double * 3)()
+            rc = lib.valu_rates_run(s, w, 20000, res)
+            if rc != 0:
+                raise RuntimeError(f"valu_rates_run({name}, {w}) returned {rc}")
+            row[f"w{w}"] = {"rate": round(res[0], 4), "ghz": round(res[1], 3), "ms": round(res[2], 3)}
+        log(row)
+        out.append(row)
+    print(json.dumps({"valu_rates": out, "unit": "wave-instructions per SIMD per shader clock"}), flush=True)
 
 
 def gemm_variants(torch, np, br, synth, dev):

@@ -20,6 +20,10 @@ PKG = os.path.dirname(HERE)
 ROOT = os.path.dirname(PKG)
 INCLUDE = os.path.join(ROOT, "include")
 LIB = os.path.join(PKG, "librepro.so")
+# Measurement support, not part of librepro: the VALU issue-rate streams that
+# bench.py --valu-rates runs.
+RATES_SRC = "valu_rates.hip"
+RATES_LIB = os.path.join(PKG, "libvalu_rates.so")
 BUILD_DIR = os.path.join(ROOT, "_build")
 
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
@@ -58,8 +62,13 @@ def _compile(src: str, extra: list[str], verbose: bool) -> str:
 
 def build(verbose: bool = False) -> str:
     os.makedirs(BUILD_DIR, exist_ok=True)
-    with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), SOURCES.items()))
+    jobs = list(SOURCES.items()) + [(RATES_SRC, [])]
+    with ThreadPoolExecutor(max_workers=len(jobs)) as ex:
+        objs = list(ex.map(lambda kv: _compile(kv[0], kv[1], verbose), jobs))
+    rates_obj = objs.pop()
+    cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", rates_obj, "-o", RATES_LIB + ".tmp"]
+    subprocess.run(cmd, check=True)
+    os.replace(RATES_LIB + ".tmp", RATES_LIB)
     cmd = [HIPCC, f"--offload-arch={ARCH}", "-shared", "-fPIC", *objs, "-o", LIB + ".tmp"]
     if verbose:
         print(" ".join(cmd), flush=True)

@@ -128,7 +128,7 @@ def test_no_kernel_uses_scratch(kernels):
 
 def test_hash_compression_instruction_mix(kernels):
     # The hash rows' bounds count ~2,000 VALU instructions per 128-byte block,
-    # 1,153 of them 8-byte encodings: per G function 6 v_lshl_add_u64 (64-bit
+    # 1,153 of them half-rate opcodes: per G function 6 v_lshl_add_u64 (64-bit
     # adds), 6 v_alignbit_b32 (rotations by 24, 16, 63; by 32 is a swap) and 8
     # v_xor_b32; 96 G per block.  Each kernel below holds one compression body
     # (k_hash_leaves<true> two: whole leaves and the word-by-word tail).
