@@ -118,7 +118,8 @@ int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
  *   variant 0: matrix cores.  v_mfma_f32_32x32x1_2b_f32 with K = 1 takes the
  *              chain value as its C operand, which is exactly one fused step
  *              per output; consecutive instructions walk k in order.
- *   variant 1: VALU, one v_fma_f32 per step (128x128 tile).
+ *   variant 1: VALU, one v_fma_f32 per step (the unfused default's tiles:
+ *              256x128 for outputs with at least 512 of them, else 128x128).
  * Both variants return the same bits.
  */
 int repro_gemm_fma(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,

@@ -174,6 +174,25 @@ def test_fused_several_tiles_with_ragged_edges(ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant={variant}")
 
 
+@pytest.mark.parametrize("K", [80, 77])
+@pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
+def test_fused_large_output_tiles_every_word(ta, tb, K):
+    # 4173 x 4141 outputs (561 tiles of 256 x 128, partial in M and N): the
+    # VALU variant takes its large-output kernel, with whole 16-deep slabs
+    # (K = 80) or a partial last one (K = 77).  Every word against the
+    # oracle's fused chains, and the matrix-core variant against it.
+    M, N = 4173, 4141
+    tid = 0x9900 + 4 * ta + 2 * tb + (K & 1)
+    A = _mat(K, M, tid) if ta else _mat(M, K, tid)
+    B = _mat(N, K, tid + 1, 0.5) if tb else _mat(K, N, tid + 1, 0.5)
+    ref = oracle.gemm(A, B, bool(ta), bool(tb), fused=True)
+    dA, dB = to_dev(A), to_dev(B)
+    C1 = br.repro_gemm_fma(dA, dB, bool(ta), bool(tb), variant=1)
+    assert_bitwise(to_host(C1), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant=1")
+    C0 = br.repro_gemm_fma(dA, dB, bool(ta), bool(tb), variant=0)
+    assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
+
+
 def test_fused_witness_and_difference_from_unfused():
     t = np.float32(1.0 + 2.0 ** -12)
     A = np.array([[-1.0, t]], np.float32)

@@ -53,6 +53,30 @@ def test_gemm_output_past_two_to_the_31():
         assert_bitwise(to_host(C[:, c]), oracle.gemm(Ah, np.ascontiguousarray(Bh[:, c:c + 1]))[:, 0], f"column {c}")
 
 
+def test_gemm_slab_offsets_past_two_to_the_32_bytes():
+    # A is a 512 x 48 view with a leading dimension of 2^22 + 4 floats (8.6 GB
+    # spanned), so a lane's byte offset inside one 256-row slab of A passes
+    # 2^32: the interior tiles cannot use 32-bit slab offsets and take the
+    # bounds-checked loads.  The result must equal the same product from a
+    # compact copy of A (interior loads) word for word, and the oracle's rows.
+    M, K, N = 512, 48, 32768  # 2 x 256 tiles of 256 x 128: the large-output kernel
+    lda = (1 << 22) + 4
+    print(f"gemm {M}x{N}x{K} lda={lda}", flush=True)
+    compact = _randn(M * K, 41, 1.0).view(M, K)
+    big = torch.empty((M - 1) * lda + K, device="cuda")
+    A = big.as_strided((M, K), (lda, 1))
+    A.copy_(compact)
+    B = _randn(K * N, 42, 1.0).view(K, N)
+    C_view = br.repro_gemm(A, B)
+    C_compact = br.repro_gemm(compact, B)
+    torch.cuda.synchronize()
+    assert torch.equal(C_view.view(torch.int32), C_compact.view(torch.int32))
+    Ah, Bh = to_host(compact), to_host(B)
+    for r in (0, 255, 256, M - 1):
+        assert_bitwise(to_host(C_view[r]), oracle.gemm(Ah[r:r + 1], Bh)[0], f"row {r}")
+    del big
+
+
 def test_state_hash_past_two_to_the_32_words():
     n = (1 << 32) + 1000  # 17.2 GB; the last leaf holds 4,000 bytes
     print(f"state hash n_words={n}", flush=True)
