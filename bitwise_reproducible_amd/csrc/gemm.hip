@@ -42,12 +42,7 @@ struct GemmTile {
   static constexpr int TX = BN / TN;  // lanes along n
   static constexpr int TY = BM / TM;  // lanes along m
   static constexpr int NT = TX * TY;  // lanes per workgroup
-  static constexpr int PAD = 4;       // keeps 16-byte alignment of LDS rows
-  static constexpr int LA = BM * BK / 4 / NT;  // 4-element chunks of A per lane per slab
-  static constexpr int LB = BK * BN / 4 / NT;
   static_assert(TM % 4 == 0 && TN % 4 == 0, "register tiles are read as 16-byte vectors");
-  static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
-  static_assert(BK % 4 == 0, "BK must be a multiple of 4");
 };
 
 // Loads one slab chunk (4 consecutive elements along the contiguous
@@ -73,28 +68,70 @@ __device__ __forceinline__ float4 load_chunk(const float* __restrict__ p, int64_
 
 typedef float v4f __attribute__((ext_vector_type(4)));
 
-template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC, bool FUSED>
-__device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
-                                          int64_t lda, const float* __restrict__ B, int64_t ldb,
-                                          float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
-  using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
-  __shared__ __attribute__((aligned(16))) float As[2][BK][BM + T::PAD];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + T::PAD];
+// Byte offsets inside one slab fit in 32 bits for these leading dimensions
+// (every lane's offset from the slab's base below 2^32 bytes).
+template <int BM, int BN, int BK, bool TA, bool TB>
+bool slab_offsets_fit(int64_t lda, int64_t ldb) {
+  const int64_t a_span = TA ? (int64_t)BK * lda + BM : (int64_t)BM * lda + BK;
+  const int64_t b_span = TB ? (int64_t)BN * ldb + BK : (int64_t)BK * ldb + BN;
+  return lda < ((int64_t)1 << 40) && ldb < ((int64_t)1 << 40) && 4 * a_span < ((int64_t)1 << 32) &&
+         4 * b_span < ((int64_t)1 << 32);
+}
 
-  const int tile = blockIdx.x;
-  const int64_t i0 = (int64_t)(tile / tiles_n) * BM;
-  const int64_t j0 = (int64_t)(tile % tiles_n) * BN;
-  const int tid = threadIdx.x;
-  const int tx = tid % T::TX;
-  const int ty = tid / T::TX;
+// Staging of the BK-deep k slabs of op(A) (BM rows) and op(B) (BN columns)
+// for a workgroup of NT lanes: global memory -> registers -> LDS, k-major in
+// LDS (double-buffered), shared by the VALU and matrix-core tiles.  Each
+// lane loads 16-byte chunks along the stored matrix's contiguous dimension.
+template <int BM, int BN, int BK, int NT, bool TA, bool TB, bool VEC>
+struct SlabStager {
+  static constexpr int PAD = 4;                // keeps 16-byte alignment of LDS rows
+  static constexpr int LA = BM * BK / 4 / NT;  // 4-element chunks of A per lane per slab
+  static constexpr int LB = BK * BN / 4 / NT;
+  static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
+  static_assert(BK % 4 == 0, "BK must be a multiple of 4");
+  typedef float ASlab[BK][BM + PAD];
+  typedef float BSlab[BK][BN + PAD];
 
-  v4f ra[T::LA], rb[T::LB];
+  ASlab* As;  // [2], in LDS
+  BSlab* Bs;
+  const float* A;
+  const float* B;
+  int64_t lda, ldb, M, N, K, i0, j0;
+  int tid;
+  // Interior tiles: a wave-uniform slab base and per-lane 32-bit offsets.
+  const char* abase;
+  const char* bbase;
+  int64_t astep, bstep;
+  uint32_t oa[LA], ob[LB];
+  v4f ra[LA], rb[LB];
+
+  __device__ __forceinline__ SlabStager(ASlab* As_, BSlab* Bs_, const float* A_, int64_t lda_, const float* B_,
+                                        int64_t ldb_, int64_t M_, int64_t N_, int64_t K_, int64_t i0_,
+                                        int64_t j0_, int tid_)
+      : As(As_), Bs(Bs_), A(A_), B(B_), lda(lda_), ldb(ldb_), M(M_), N(N_), K(K_), i0(i0_), j0(j0_), tid(tid_) {
+#pragma unroll
+    for (int q = 0; q < LA; ++q) {
+      const int f = tid + q * NT;
+      oa[q] = !TA ? (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * lda + 4 * (f % (BK / 4))))
+                  : (uint32_t)(4 * ((int64_t)(f / (BM / 4)) * lda + 4 * (f % (BM / 4))));
+    }
+#pragma unroll
+    for (int q = 0; q < LB; ++q) {
+      const int f = tid + q * NT;
+      ob[q] = !TB ? (uint32_t)(4 * ((int64_t)(f / (BN / 4)) * ldb + 4 * (f % (BN / 4))))
+                  : (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * ldb + 4 * (f % (BK / 4))));
+    }
+    abase = reinterpret_cast<const char*>(TA ? A + i0 : A + i0 * lda);
+    bbase = reinterpret_cast<const char*>(TB ? B + j0 * ldb : B + j0);
+    astep = 4 * (TA ? BK * lda : BK);
+    bstep = 4 * (TB ? BK : BK * ldb);
+  }
 
   // Global -> registers for the slab starting at k0, bounds-checked.
-  auto load_slab = [&](int64_t k0) __attribute__((always_inline)) {
+  __device__ __forceinline__ void load_checked(int64_t k0) {
 #pragma unroll
-    for (int q = 0; q < T::LA; ++q) {
-      const int f = tid + q * T::NT;
+    for (int q = 0; q < LA; ++q) {
+      const int f = tid + q * NT;
       float4 v;
       if constexpr (!TA) {  // A is M x K row-major: rows i, contiguous k
         const int r = f / (BK / 4), c4 = f % (BK / 4);
@@ -106,8 +143,8 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
       ra[q] = v4f{v.x, v.y, v.z, v.w};
     }
 #pragma unroll
-    for (int q = 0; q < T::LB; ++q) {
-      const int f = tid + q * T::NT;
+    for (int q = 0; q < LB; ++q) {
+      const int f = tid + q * NT;
       float4 v;
       if constexpr (!TB) {  // B is K x N row-major: rows k, contiguous j
         const int c = f / (BN / 4), j4 = f % (BN / 4);
@@ -118,44 +155,23 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
       }
       rb[q] = v4f{v.x, v.y, v.z, v.w};
     }
-  };
+  }
 
-  // Interior tiles (the whole BM x BN tile inside C, 16-byte rows, and every
-  // lane's offset inside a slab below 2^32 bytes): each lane's offsets are
-  // formed once, the slab base advances as a wave-uniform 64-bit address,
-  // and the loads carry no bounds checks.
-  const bool interior = VEC && off32 && i0 + BM <= M && j0 + BN <= N;
-  uint32_t oa[T::LA], ob[T::LB];
-#pragma unroll
-  for (int q = 0; q < T::LA; ++q) {
-    const int f = tid + q * T::NT;
-    oa[q] = !TA ? (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * lda + 4 * (f % (BK / 4))))
-                : (uint32_t)(4 * ((int64_t)(f / (BM / 4)) * lda + 4 * (f % (BM / 4))));
-  }
-#pragma unroll
-  for (int q = 0; q < T::LB; ++q) {
-    const int f = tid + q * T::NT;
-    ob[q] = !TB ? (uint32_t)(4 * ((int64_t)(f / (BN / 4)) * ldb + 4 * (f % (BN / 4))))
-                : (uint32_t)(4 * ((int64_t)(f / (BK / 4)) * ldb + 4 * (f % (BK / 4))));
-  }
-  const char* const abase = reinterpret_cast<const char*>(TA ? A + i0 : A + i0 * lda);
-  const char* const bbase = reinterpret_cast<const char*>(TB ? B + j0 * ldb : B + j0);
-  const int64_t astep = 4 * (TA ? BK * lda : BK);
-  const int64_t bstep = 4 * (TB ? BK : BK * ldb);
-  auto load_slab_interior = [&](int64_t s) __attribute__((always_inline)) {
+  // Global -> registers for slab s of an interior tile: no bounds checks.
+  __device__ __forceinline__ void load_interior(int64_t s) {
     const char* ab = abase + s * astep;
     const char* bb = bbase + s * bstep;
 #pragma unroll
-    for (int q = 0; q < T::LA; ++q) ra[q] = *reinterpret_cast<const v4f*>(ab + oa[q]);
+    for (int q = 0; q < LA; ++q) ra[q] = *reinterpret_cast<const v4f*>(ab + oa[q]);
 #pragma unroll
-    for (int q = 0; q < T::LB; ++q) rb[q] = *reinterpret_cast<const v4f*>(bb + ob[q]);
-  };
+    for (int q = 0; q < LB; ++q) rb[q] = *reinterpret_cast<const v4f*>(bb + ob[q]);
+  }
 
-  // Registers -> LDS, k-major.
-  auto store_slab = [&](int buf) __attribute__((always_inline)) {
+  // Registers -> LDS buffer `buf`, k-major.
+  __device__ __forceinline__ void store(int buf) {
 #pragma unroll
-    for (int q = 0; q < T::LA; ++q) {
-      const int f = tid + q * T::NT;
+    for (int q = 0; q < LA; ++q) {
+      const int f = tid + q * NT;
       if constexpr (!TA) {
         const int r = f / (BK / 4), c4 = f % (BK / 4);
         As[buf][4 * c4 + 0][r] = ra[q].x;
@@ -168,8 +184,8 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
       }
     }
 #pragma unroll
-    for (int q = 0; q < T::LB; ++q) {
-      const int f = tid + q * T::NT;
+    for (int q = 0; q < LB; ++q) {
+      const int f = tid + q * NT;
       if constexpr (!TB) {
         const int c = f / (BN / 4), j4 = f % (BN / 4);
         *reinterpret_cast<v4f*>(&Bs[buf][c][4 * j4]) = rb[q];
@@ -181,7 +197,70 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
         Bs[buf][4 * c4 + 3][j] = rb[q].w;
       }
     }
+  }
+};
+
+// The k loop of a tile: slabs 0 .. K/BK - 1 are full, a last, partial one
+// holds K % BK steps; `full_slab(buf)` runs the BK steps of a staged slab in
+// ascending order and `step(buf, kk)` one step.  Interior tiles (the whole
+// tile inside C, 16-byte rows, 32-bit slab offsets, K a whole number of
+// slabs) and the others run separate copies of the loop: the same steps in
+// the same order, other loads.  The loop body is the same on every pass (a
+// conditional prefetch makes the compiler spill): an interior tile reloads
+// its last slab on the last pass and the bounds-checked loads read past K
+// as zeros, into the buffer that is no longer read.
+template <int BK, class Stager, class FullSlab, class Step>
+__device__ __forceinline__ void run_k_loop(Stager& st, bool interior, int64_t K, FullSlab full_slab, Step step) {
+  const int64_t nfull = K / BK;
+  auto run = [&](auto interior_tag) __attribute__((always_inline)) {
+    constexpr bool kInterior = decltype(interior_tag)::value;
+    if constexpr (kInterior) {
+      st.load_interior(0);
+    } else {
+      st.load_checked(0);
+    }
+    st.store(0);
+    __syncthreads();
+    int buf = 0;
+    for (int64_t s = 0; s < nfull; ++s) {
+      if constexpr (kInterior) {
+        st.load_interior(s + 1 < nfull ? s + 1 : s);
+      } else {
+        st.load_checked((s + 1) * BK);
+      }
+      full_slab(buf);
+      st.store(buf ^ 1);
+      __syncthreads();
+      buf ^= 1;
+    }
+    if constexpr (!kInterior) {
+      const int kleft = (int)(K - nfull * BK);
+      for (int kk = 0; kk < kleft; ++kk) step(buf, kk);
+    }
   };
+  if (interior && K % BK == 0 && nfull > 0) {
+    run(std::true_type{});
+  } else if (K > 0) {
+    run(std::false_type{});
+  }
+}
+
+template <int BM, int BN, int BK, int TM, int TN, bool TA, bool TB, bool VEC, bool FUSED>
+__device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
+                                          int64_t lda, const float* __restrict__ B, int64_t ldb,
+                                          float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
+  using T = GemmTile<BM, BN, BK, TM, TN, TA, TB, VEC>;
+  using S = SlabStager<BM, BN, BK, T::NT, TA, TB, VEC>;
+  __shared__ __attribute__((aligned(16))) typename S::ASlab As[2];
+  __shared__ __attribute__((aligned(16))) typename S::BSlab Bs[2];
+
+  const int tile = blockIdx.x;
+  const int64_t i0 = (int64_t)(tile / tiles_n) * BM;
+  const int64_t j0 = (int64_t)(tile % tiles_n) * BN;
+  const int tid = threadIdx.x;
+  const int tx = tid % T::TX;
+  const int ty = tid / T::TX;
+  S st(As, Bs, A, lda, B, ldb, M, N, K, i0, j0, tid);
 
   float acc[TM][TN];
 #pragma unroll
@@ -230,51 +309,12 @@ __device__ __forceinline__ void gemm_tile(int64_t M, int64_t N, int64_t K, const
       __builtin_amdgcn_sched_barrier(0);
     }
   };
-
-  // Slabs 0 .. nfull-1 are full; a last, partial one holds K - nfull * BK
-  // steps.  Interior tiles (which need K to be a whole number of slabs) and
-  // the others run separate copies of the slab loop: the same steps in the
-  // same order, other loads.
-  const int64_t nfull = K / BK;
-  const int64_t nslabs = (K + BK - 1) / BK;
-  auto run = [&](auto interior_tag) __attribute__((always_inline)) {
-    constexpr bool kInterior = decltype(interior_tag)::value;
-    if constexpr (kInterior) {
-      load_slab_interior(0);
-    } else {
-      load_slab(0);
-    }
-    store_slab(0);
-    __syncthreads();
-    int buf = 0;
-    // The loop body is the same on every pass (a conditional prefetch makes
-    // the compiler spill): an interior tile reloads its last slab on the
-    // last pass, the bounds-checked loads read past K as zeros.  Either way
-    // the extra slab lands in the buffer that is no longer read.
-    for (int64_t s = 0; s < nfull; ++s) {
-      if constexpr (kInterior) {
-        load_slab_interior(s + 1 < nfull ? s + 1 : s);
-      } else {
-        load_slab((s + 1) * BK);
-      }
-      full_slab(buf);
-      store_slab(buf ^ 1);
-      __syncthreads();
-      buf ^= 1;
-    }
-    if constexpr (!kInterior) {
-      const int kleft = (int)(K - nfull * BK);
-      for (int kk = 0; kk < kleft; ++kk) {
-        read_frag(0, buf, kk);
-        mac_frag(0);
-      }
-    }
+  auto step = [&](int buf, int kk) __attribute__((always_inline)) {
+    read_frag(0, buf, kk);
+    mac_frag(0);
   };
-  if (interior && K % BK == 0 && nfull > 0) {
-    run(std::true_type{});
-  } else if (nslabs > 0) {
-    run(std::false_type{});
-  }
+  const bool interior = VEC && off32 && i0 + BM <= M && j0 + BN <= N;
+  run_k_loop<BK>(st, interior, K, full_slab, step);
 
   // Epilogue: lane rows g*4*TY + ty*4 + e, columns h*4*TX + tx*4 + 0..3.
   const bool vec_c = VEC && (ldc % 4 == 0) && ((reinterpret_cast<uintptr_t>(C) & 15u) == 0);
@@ -344,12 +384,11 @@ typedef float floatx32 __attribute__((ext_vector_type(32)));
 template <int BK, bool TA, bool TB, bool VEC, bool FUSED>
 __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
                                                int64_t lda, const float* __restrict__ B, int64_t ldb,
-                                               float* __restrict__ C, int64_t ldc, int tiles_n) {
-  constexpr int BM = 128, BN = 128, NT = 256, PAD = 4;
-  constexpr int LA = BM * BK / 4 / NT, LB = BK * BN / 4 / NT;
-  static_assert(LA * NT * 4 == BM * BK && LB * NT * 4 == BK * BN, "slab must split evenly over lanes");
-  __shared__ __attribute__((aligned(16))) float As[2][BK][BM + PAD];
-  __shared__ __attribute__((aligned(16))) float Bs[2][BK][BN + PAD];
+                                               float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
+  constexpr int BM = 128, BN = 128, NT = 256;
+  using S = SlabStager<BM, BN, BK, NT, TA, TB, VEC>;
+  __shared__ __attribute__((aligned(16))) typename S::ASlab As[2];
+  __shared__ __attribute__((aligned(16))) typename S::BSlab Bs[2];
 
   const int tile = blockIdx.x;
   const int64_t i0 = (int64_t)(tile / tiles_n) * BM;
@@ -359,62 +398,7 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
   const int wave = tid >> 6;
   const int wm = (wave >> 1) * 64;  // wave's first row inside the tile
   const int wn = (wave & 1) * 64;   // wave's first column inside the tile
-
-  float4 ra[LA], rb[LB];
-  auto load_slab = [&](int64_t k0) {
-#pragma unroll
-    for (int q = 0; q < LA; ++q) {
-      const int f = tid + q * NT;
-      if constexpr (!TA) {
-        const int r = f / (BK / 4), c4 = f % (BK / 4);
-        ra[q] = load_chunk<VEC>(A, i0 + r, k0 + 4 * c4, lda, M, K);
-      } else {
-        const int c = f / (BM / 4), r4 = f % (BM / 4);
-        ra[q] = load_chunk<VEC>(A, k0 + c, i0 + 4 * r4, lda, K, M);
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < LB; ++q) {
-      const int f = tid + q * NT;
-      if constexpr (!TB) {
-        const int c = f / (BN / 4), j4 = f % (BN / 4);
-        rb[q] = load_chunk<VEC>(B, k0 + c, j0 + 4 * j4, ldb, K, N);
-      } else {
-        const int j = f / (BK / 4), c4 = f % (BK / 4);
-        rb[q] = load_chunk<VEC>(B, j0 + j, k0 + 4 * c4, ldb, N, K);
-      }
-    }
-  };
-  auto store_slab = [&](int buf) {
-#pragma unroll
-    for (int q = 0; q < LA; ++q) {
-      const int f = tid + q * NT;
-      if constexpr (!TA) {
-        const int r = f / (BK / 4), c4 = f % (BK / 4);
-        As[buf][4 * c4 + 0][r] = ra[q].x;
-        As[buf][4 * c4 + 1][r] = ra[q].y;
-        As[buf][4 * c4 + 2][r] = ra[q].z;
-        As[buf][4 * c4 + 3][r] = ra[q].w;
-      } else {
-        const int c = f / (BM / 4), r4 = f % (BM / 4);
-        *reinterpret_cast<float4*>(&As[buf][c][4 * r4]) = ra[q];
-      }
-    }
-#pragma unroll
-    for (int q = 0; q < LB; ++q) {
-      const int f = tid + q * NT;
-      if constexpr (!TB) {
-        const int c = f / (BN / 4), j4 = f % (BN / 4);
-        *reinterpret_cast<float4*>(&Bs[buf][c][4 * j4]) = rb[q];
-      } else {
-        const int j = f / (BK / 4), c4 = f % (BK / 4);
-        Bs[buf][4 * c4 + 0][j] = rb[q].x;
-        Bs[buf][4 * c4 + 1][j] = rb[q].y;
-        Bs[buf][4 * c4 + 2][j] = rb[q].z;
-        Bs[buf][4 * c4 + 3][j] = rb[q].w;
-      }
-    }
-  };
+  S st(As, Bs, A, lda, B, ldb, M, N, K, i0, j0, tid);
 
   floatx32 acc0, acc1, negz;
 #pragma unroll
@@ -423,7 +407,7 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
     acc1[r] = 0.0f;
     negz[r] = -0.0f;
   }
-  auto mac_step = [&](int buf, int kk) {
+  auto mac_step = [&](int buf, int kk) __attribute__((always_inline)) {
     const float a = As[buf][kk][wm + lane];
     const float b0 = Bs[buf][kk][wn + (lane & 31)];
     const float b1 = Bs[buf][kk][wn + 32 + (lane & 31)];
@@ -441,25 +425,14 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
     }
   };
 
-  const int64_t nslabs = (K + BK - 1) / BK;
-  if (nslabs > 0) {
-    load_slab(0);
-    store_slab(0);
-    __syncthreads();
-    for (int64_t s = 0; s < nslabs; ++s) {
-      const int buf = (int)(s & 1);
-      if (s + 1 < nslabs) load_slab((s + 1) * BK);
-      const int64_t kleft = K - s * BK;
-      if (kleft >= BK) {
+  auto full_slab = [&](int buf) __attribute__((always_inline)) {
 #pragma unroll
-        for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
-      } else {
-        for (int kk = 0; kk < (int)kleft; ++kk) mac_step(buf, kk);
-      }
-      if (s + 1 < nslabs) store_slab(buf ^ 1);
-      __syncthreads();
-    }
-  }
+    for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
+  };
+  // The unfused form keeps to the bounds-checked loop: with the interior
+  // copy as well its pipelined products need more than 256 VGPRs.
+  const bool interior = FUSED && VEC && off32 && i0 + BM <= M && j0 + BN <= N;
+  run_k_loop<BK>(st, interior, K, full_slab, mac_step);
 
   // Register r of a lane holds row 32*(r/16) + 8*((r%16)/4) + 4*(lane/32) + r%4
   // of the wave tile, column lane%32 (+32 for the second instruction).
@@ -478,8 +451,8 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
 template <int BK, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void k_gemm_mfma(int64_t M, int64_t N, int64_t K, const float* __restrict__ A,
                                                    int64_t lda, const float* __restrict__ B, int64_t ldb,
-                                                   float* __restrict__ C, int64_t ldc, int tiles_n) {
-  gemm_mfma_tile<BK, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+                                                   float* __restrict__ C, int64_t ldc, int tiles_n, int off32) {
+  gemm_mfma_tile<BK, TA, TB, VEC, false>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n, off32);
 }
 
 // The fused convention on the matrix cores: v_mfma_f32_32x32x1_2b_f32 with
@@ -490,8 +463,9 @@ template <int BK, bool TA, bool TB, bool VEC>
 __global__ __launch_bounds__(256) void k_gemm_mfma_fma(int64_t M, int64_t N, int64_t K,
                                                        const float* __restrict__ A, int64_t lda,
                                                        const float* __restrict__ B, int64_t ldb,
-                                                       float* __restrict__ C, int64_t ldc, int tiles_n) {
-  gemm_mfma_tile<BK, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n);
+                                                       float* __restrict__ C, int64_t ldc, int tiles_n,
+                                                       int off32) {
+  gemm_mfma_tile<BK, TA, TB, VEC, true>(M, N, K, A, lda, B, ldb, C, ldc, tiles_n, off32);
 }
 
 template <int BK, bool TA, bool TB, bool VEC, bool FUSED>
@@ -501,12 +475,13 @@ hipError_t launch_mfma(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
   const int64_t tiles_n = (N + 127) / 128;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
+  const int off32 = slab_offsets_fit<128, 128, BK, TA, TB>(lda, ldb) ? 1 : 0;
   if constexpr (FUSED)
     hipLaunchKernelGGL((k_gemm_mfma_fma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A,
-                       lda, B, ldb, C, ldc, (int)tiles_n);
+                       lda, B, ldb, C, ldc, (int)tiles_n, off32);
   else
     hipLaunchKernelGGL((k_gemm_mfma<BK, TA, TB, VEC>), dim3((unsigned)tiles), dim3(256), 0, stream, M, N, K, A,
-                       lda, B, ldb, C, ldc, (int)tiles_n);
+                       lda, B, ldb, C, ldc, (int)tiles_n, off32);
   return hipGetLastError();
 }
 
@@ -535,12 +510,8 @@ hipError_t launch_tiled(int64_t M, int64_t N, int64_t K, const float* A, int64_t
   const int64_t tiles_n = (N + BN - 1) / BN;
   const int64_t tiles = tiles_m * tiles_n;
   if (tiles > 0x7fffffff) return hipErrorInvalidValue;
-  // Largest byte offset of a lane inside one slab, from the slab's base:
-  // interior tiles address slabs with 32-bit lane offsets when it fits.
-  const int64_t a_span = TA ? (int64_t)BK * lda + BM : (int64_t)BM * lda + BK;
-  const int64_t b_span = TB ? (int64_t)BN * ldb + BK : (int64_t)BK * ldb + BN;
-  const int off32 = (lda < ((int64_t)1 << 40) && ldb < ((int64_t)1 << 40) && 4 * a_span < ((int64_t)1 << 32) &&
-                     4 * b_span < ((int64_t)1 << 32)) ? 1 : 0;
+  // Interior tiles address slabs with 32-bit lane offsets when they fit.
+  const int off32 = slab_offsets_fit<BM, BN, BK, TA, TB>(lda, ldb) ? 1 : 0;
   if constexpr (FUSED)
     hipLaunchKernelGGL((k_gemm_fma<BM, BN, BK, TM, TN, TA, TB, VEC>), dim3((unsigned)tiles), dim3(T::NT), 0,
                        stream, M, N, K, A, lda, B, ldb, C, ldc, (int)tiles_n, off32);
