@@ -154,3 +154,49 @@ def test_captured_no_allocation_update_and_hash():
         oracle.adamw_inplace(ref, g, **hp)
     assert_bitwise(to_host(cap_state), ref, "state after three replays")
     assert bytes(to_host(cap_digest).tobytes()) == oracle.state_hash(ref)
+
+
+def test_captured_gemms_with_interior_tiles():
+    # GEMMs whose interior tiles take the unchecked slab loads, captured and
+    # replayed: 512 x 640 x 96 (128 x 128 tiles), 4096 x 4096 x 32 (512 tiles
+    # of 256 x 128, the large-output kernel) and the fused convention on the
+    # matrix cores, dW-style (trans_a).  Three replays, each against the same
+    # calls made eagerly, then the oracle.
+    shapes = [(512, 640, 96, 0, "unfused"), (4096, 4096, 32, 0, "unfused"), (512, 512, 64, 1, "fused")]
+    ins = []
+    for i, (M, N, K, ta, conv) in enumerate(shapes):
+        A = synth.generate(M * K, synth.NORMAL, synth.tid(8, 0x30 + 2 * i), 1.0).reshape((K, M) if ta else (M, K))
+        B = synth.generate(K * N, synth.NORMAL, synth.tid(8, 0x31 + 2 * i), 0.5).reshape(K, N)
+        ins.append((A, B, to_dev(A), to_dev(B)))
+
+    def run(outs):
+        for (M, N, K, ta, conv), (_, _, dA, dB), C in zip(shapes, ins, outs):
+            if conv == "fused":
+                br.repro_gemm_fma(dA, dB, bool(ta), False, out=C, variant=0)
+            else:
+                br.repro_gemm(dA, dB, bool(ta), False, out=C)
+
+    new = lambda: [torch.empty(M, N, device="cuda") for (M, N, _, _, _) in shapes]
+    cap, eager, warm = new(), new(), new()
+    side = torch.cuda.Stream()
+    side.wait_stream(torch.cuda.current_stream())
+    with torch.cuda.stream(side):
+        run(warm)
+    torch.cuda.current_stream().wait_stream(side)
+    torch.cuda.synchronize()
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.graph(graph):
+        run(cap)
+    torch.cuda.synchronize()
+    for k in range(3):
+        for C in cap:
+            C.fill_(float("nan"))  # a replay must rewrite every word
+        torch.cuda.synchronize()
+        graph.replay()
+        run(eager)
+        torch.cuda.synchronize()
+        for i, (C, E) in enumerate(zip(cap, eager)):
+            assert torch.equal(C.view(torch.int32), E.view(torch.int32)), f"replay {k}: gemm {shapes[i]}"
+    for (M, N, K, ta, conv), (A, B, _, _), C in zip(shapes, ins, cap):
+        ref = oracle.gemm(A, B, bool(ta), False, fused=(conv == "fused"))
+        assert_bitwise(to_host(C), ref, f"gemm {M}x{N}x{K} ta={ta} {conv}")
