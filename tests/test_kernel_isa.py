@@ -119,6 +119,44 @@ def test_unfused_gemm_chain_is_one_multiply_and_one_add_per_step(kernels):
     assert seen == 8
 
 
+def _loops(body: str):
+    """Instruction counts of each loop (a label and the branch back to it)."""
+    lines = body.split("\n")
+    out = []
+    for i, line in enumerate(lines):
+        m = re.match(r"(\.LBB\d+_\d+):", line)
+        if not m:
+            continue
+        for j in range(i + 1, len(lines)):
+            if re.search(r"s_(cbranch_\w+|branch) " + re.escape(m.group(1)) + r"$", lines[j]):
+                out.append(Counter(re.findall(r"^\s+([a-z_0-9]+)", "\n".join(lines[i:j]), re.M)))
+                break
+    return out
+
+
+def test_interior_slab_loop_is_branch_free():
+    # The VALU GEMMs with 16-byte loads run interior tiles through a slab loop
+    # with unchecked loads from a uniform base: no exec-mask branches, no
+    # register copies (a join of two compute paths in the loop once copied
+    # every accumulator on each pass), one 64-bit address add per load.
+    asm = lib_build.disassemble("gemm.hip")
+    seen = 0
+    for part in re.split(r"\n(?=_Z[^\s:]+:)", asm):
+        m = re.match(r"(_Z[^\s:]+):", part)
+        if not m or not re.search(r"k_gemm(_fma)?ILi(256|128)ELi128E.*ELb1EEEv", m.group(1)):
+            continue
+        loops = _loops(part.split(".Lfunc_end")[0])
+        interior = [c for c in loops if c["v_mul_f32_e32"] + c["v_fmac_f32_e32"] + c["v_fma_f32"] >= 2048
+                    and c["s_and_saveexec_b64"] == 0]
+        assert len(interior) == 1, (_short(m.group(1)), m.group(1))
+        c = interior[0]
+        assert c["v_mov_b32_e32"] == 0, (m.group(1), c["v_mov_b32_e32"])
+        assert 1 <= c["global_load_dwordx4"] <= 8 and c["v_lshl_add_u64"] <= c["global_load_dwordx4"] + 2, (
+            m.group(1), c)
+        seen += 1
+    assert seen == 16  # k_gemm and k_gemm_fma, two tile shapes, 4 transposes each
+
+
 def test_no_kernel_uses_scratch(kernels):
     ks, meta = kernels
     assert set(meta) >= set(ks)
