@@ -43,11 +43,15 @@ def _short(mangled: str) -> str:
 
 
 @pytest.fixture(scope="module")
-def kernels():
+def asms():
     with ThreadPoolExecutor(max_workers=len(SOURCES)) as ex:
-        asms = list(ex.map(lib_build.disassemble, SOURCES))
+        return dict(zip(SOURCES, ex.map(lib_build.disassemble, SOURCES)))
+
+
+@pytest.fixture(scope="module")
+def kernels(asms):
     ks, meta = {}, {}
-    for a in asms:
+    for a in asms.values():
         k, m = _kernels(a)
         ks.update(k)
         meta.update(m)
@@ -134,12 +138,12 @@ def _loops(body: str):
     return out
 
 
-def test_interior_slab_loop_is_branch_free():
+def test_interior_slab_loop_is_branch_free(asms):
     # The VALU GEMMs with 16-byte loads run interior tiles through a slab loop
     # with unchecked loads from a uniform base: no exec-mask branches, no
     # register copies (a join of two compute paths in the loop once copied
     # every accumulator on each pass), one 64-bit address add per load.
-    asm = lib_build.disassemble("gemm.hip")
+    asm = asms["gemm.hip"]
     seen = 0
     for part in re.split(r"\n(?=_Z[^\s:]+:)", asm):
         m = re.match(r"(_Z[^\s:]+):", part)
