@@ -74,6 +74,19 @@ def test_large_output_tiles_every_word(ta, tb, K):
     assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 16), (4096, 4096, 8), (4096, 4096, 1), (512, 640, 32)])
+def test_slab_count_edges(M, N, K):
+    # Interior tiles with a single whole slab (K = 16 on the 256 x 128 kernel,
+    # K = 32 on the 128 x 128 one), a single partial slab (K = 8) and K = 1:
+    # every output word against the oracle, default variant and variant 1.
+    A, B = _stored(M, N, K, 0, 0, 0x8A00 + K + (M & 7))
+    ref = oracle.gemm(A, B)
+    dA, dB = to_dev(A), to_dev(B)
+    for variant in (0, 1):
+        C = br.repro_gemm(dA, dB, variant=variant)
+        assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} variant={variant}")
+
+
 def test_tiny_workload():
     a, b = synth.tiny_gemm_inputs()
     C = br.repro_gemm(to_dev(a), to_dev(b))
