@@ -193,6 +193,21 @@ def test_fused_large_output_tiles_every_word(ta, tb, K):
     assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
 
 
+@pytest.mark.parametrize("M,N,K", [(1024, 1024, 32), (1024, 1024, 64), (4096, 4096, 16), (1024, 512, 1)])
+def test_fused_slab_count_edges(M, N, K):
+    # Interior tiles with one or two whole 32-deep slabs on the matrix cores,
+    # one whole 16-deep slab on the VALU kernel's large-output tiles, K = 1:
+    # every word against the oracle's fused chains, both variants.
+    tid = 0x9A00 + K + (M >> 10)
+    A = _mat(M, K, tid)
+    B = _mat(K, N, tid + 1, 0.5)
+    ref = oracle.gemm(A, B, fused=True)
+    dA, dB = to_dev(A), to_dev(B)
+    for variant in (0, 1):
+        C = br.repro_gemm_fma(dA, dB, variant=variant)
+        assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} fused variant={variant}")
+
+
 def test_fused_witness_and_difference_from_unfused():
     t = np.float32(1.0 + 2.0 ** -12)
     A = np.array([[-1.0, t]], np.float32)
