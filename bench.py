@@ -44,7 +44,10 @@ FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
 # lane-operations/s (the vendor fp32 figure is this rate times 2 flops per
 # FMA), i.e. 0.5 wave-instructions per SIMD per clock.  The declared MAC is a
 # multiply and an add, two lane-ops for two flops, so the GEMM's ceiling is
-# 78.6 TFLOP/s.  Full-rate opcodes (v_mul_f32, v_add_f32, v_xor_b32,
+# 78.6 TFLOP/s.  The default GEMM forms the products on the matrix cores
+# (one v_mfma_f32_32x32x1_2b_f32 per 2048 products, 64 busy cycles) and adds
+# them on the VALU; the two units take turns (co-execution counter 0), so per
+# SIMD 2048 MACs cost 64 + 64 cycles, the same 78.6 TFLOP/s ceiling.  Full-rate opcodes (v_mul_f32, v_add_f32, v_xor_b32,
 # v_lshrrev_b32, ...) reach it in either encoding; `bench.py --valu-rates`
 # measures 0.47-0.48 for long streams of them.
 VALU_LANE_OPS = 256 * 128 * 2.4e9
@@ -114,8 +117,9 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the oracle check after timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--gemm-variants", action="store_true",
-                   help="only the forward GEMM workload, once each with repro_gemm variant 0 (VALU), variant 3 "
-                        "(matrix-core products, VALU adds) and repro_gemm_fma variant 0 (matrix cores), after one "
+                   help="only the forward GEMM workload, once each with repro_gemm variant 0 (the default: "
+                        "matrix-core products, VALU adds), variant 4 (VALU multiply and add) and repro_gemm_fma "
+                        "variant 0 (matrix cores), after one "
                         "warm-up each: the run the matrix-core co-execution counters are taken on")
     p.add_argument("--valu-rates", action="store_true",
                    help="only the VALU issue-rate streams of libvalu_rates.so (single-opcode streams and the "
@@ -531,14 +535,15 @@ def valu_rates():
 
 
 def gemm_variants(torch, np, br, synth, dev):
-    """The forward GEMM workload through the unfused VALU kernel, the unfused
-    kernel with matrix-core products, and the fused matrix-core kernel."""
+    """The forward GEMM workload through the default kernel (matrix-core
+    products, VALU adds), the VALU multiply-and-add kernel, and the fused
+    matrix-core kernel."""
     GC = synth.GEMM
     X = torch.from_numpy(synth.gemm_x()).to(dev).view(GC["M"], GC["K"])
     W = torch.from_numpy(synth.gemm_w()).to(dev).view(GC["K"], GC["N"])
     Y = torch.empty(GC["M"], GC["N"], dtype=torch.float32, device=dev)
     runs = {"repro_gemm_variant0": lambda: br.repro_gemm(X, W, out=Y, variant=0),
-            "repro_gemm_variant3": lambda: br.repro_gemm(X, W, out=Y, variant=3),
+            "repro_gemm_variant4": lambda: br.repro_gemm(X, W, out=Y, variant=4),
             "repro_gemm_fma_variant0": lambda: br.repro_gemm_fma(X, W, out=Y, variant=0)}
     out = {}
     for name, call in runs.items():

@@ -100,7 +100,7 @@ namespace {
 
 int gemm_checked(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                  const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant, bool fused, void* stream) {
-  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > (fused ? 1 : 3)) return REPRO_EINVAL;
+  if (M < 0 || N < 0 || K < 0 || variant < 0 || variant > (fused ? 1 : 4)) return REPRO_EINVAL;
   if ((trans_a != 0 && trans_a != 1) || (trans_b != 0 && trans_b != 1)) return REPRO_EINVAL;
   if (M == 0 || N == 0) return REPRO_OK;
   if (C == nullptr || ldc < N) return REPRO_EINVAL;

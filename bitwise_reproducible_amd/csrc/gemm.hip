@@ -407,10 +407,8 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
     acc1[r] = 0.0f;
     negz[r] = -0.0f;
   }
-  auto mac_step = [&](int buf, int kk) __attribute__((always_inline)) {
-    const float a = As[buf][kk][wm + lane];
-    const float b0 = Bs[buf][kk][wn + (lane & 31)];
-    const float b1 = Bs[buf][kk][wn + 32 + (lane & 31)];
+  // One k step on operands already in registers.
+  auto mfma_step = [&](float a, float b0, float b1) __attribute__((always_inline)) {
     if constexpr (FUSED) {
       // The chain value is the C operand: acc = fl(a * b + acc), one rounding.
       acc0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b0, acc0, 0, 0, 0);
@@ -424,14 +422,31 @@ __device__ __forceinline__ void gemm_mfma_tile(int64_t M, int64_t N, int64_t K, 
       for (int r = 0; r < 32; ++r) acc1[r] = acc1[r] + p1[r];
     }
   };
-
-  auto full_slab = [&](int buf) __attribute__((always_inline)) {
-#pragma unroll
-    for (int kk = 0; kk < BK; ++kk) mac_step(buf, kk);
+  auto mac_step = [&](int buf, int kk) __attribute__((always_inline)) {
+    mfma_step(As[buf][kk][wm + lane], Bs[buf][kk][wn + (lane & 31)], Bs[buf][kk][wn + 32 + (lane & 31)]);
   };
-  // The unfused form keeps to the bounds-checked loop: with the interior
-  // copy as well its pipelined products need more than 256 VGPRs.
-  const bool interior = FUSED && VEC && off32 && i0 + BM <= M && j0 + BN <= N;
+  // A full slab: the operands of step kk + 1 are read from LDS before the
+  // matrix instructions of step kk are issued (held in place by scheduling
+  // barriers), so the matrix pipe does not wait on LDS latency between steps.
+  auto full_slab = [&](int buf) __attribute__((always_inline)) {
+    float op[2][3];
+    op[0][0] = As[buf][0][wm + lane];
+    op[0][1] = Bs[buf][0][wn + (lane & 31)];
+    op[0][2] = Bs[buf][0][wn + 32 + (lane & 31)];
+#pragma unroll
+    for (int kk = 0; kk < BK; ++kk) {
+      if (kk + 1 < BK) {
+        const int nx = (kk + 1) & 1;
+        op[nx][0] = As[buf][kk + 1][wm + lane];
+        op[nx][1] = Bs[buf][kk + 1][wn + (lane & 31)];
+        op[nx][2] = Bs[buf][kk + 1][wn + 32 + (lane & 31)];
+      }
+      __builtin_amdgcn_sched_barrier(0);
+      mfma_step(op[kk & 1][0], op[kk & 1][1], op[kk & 1][2]);
+      __builtin_amdgcn_sched_barrier(0);
+    }
+  };
+  const bool interior = VEC && off32 && i0 + BM <= M && j0 + BN <= N;
   run_k_loop<BK>(st, interior, K, full_slab, mac_step);
 
   // Register r of a lane holds row 32*(r/16) + 8*((r%16)/4) + 4*(lane/32) + r%4
@@ -563,21 +578,30 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
       return dispatch<256, 128, 16, 16, 8, true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
     return dispatch<128, 128, 32, 8, 8, true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   }
+  // Variant 0, the default, and variant 3: products on the matrix cores,
+  // adds on the VALU (k_gemm_mfma).  The matrix cores and the VALU take
+  // turns on this chip, so per MAC this costs what the VALU's multiply and
+  // add cost; but with half the VALU instructions the kernel runs at a
+  // higher clock, and measured on MI355X it is 0-10% faster than the VALU
+  // kernel on both GEMM workloads, with the same bits.
+  if (variant == 0 || variant == 3)
+    return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   if (variant == 2)
     return dispatch<64, 64, 16, 4, 4, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  if (variant == 3) return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  // Large outputs: 256 x 128 tiles, 16 x 8 outputs per lane, 16-deep slabs
-  // (250 VGPRs: two waves per SIMD; 50 KB of LDS).  Each k step reads 24
-  // values from LDS for 128 MACs instead of 16 for 64, and each slab moves
-  // half as many A and B bytes per MAC; measured on MI355X 3-4% faster than
-  // 128 x 128 tiles on both GEMM workloads, same bits.  Used when there are
-  // at least two such tiles per CU, so the larger tile costs no parallelism.
-  if (variant == 0 && ((M + 255) / 256) * ((N + 127) / 128) >= 512)
+  // Variant 4, the VALU multiply and add, on large outputs: 256 x 128 tiles,
+  // 16 x 8 outputs per lane, 16-deep slabs (250 VGPRs: two waves per SIMD;
+  // 50 KB of LDS).  Each k step reads 24 values from LDS for 128 MACs
+  // instead of 16 for 64, and each slab moves half as many A and B bytes per
+  // MAC; measured on MI355X 3-4% faster than 128 x 128 tiles on both GEMM
+  // workloads, same bits.  Used when there are at least two such tiles per
+  // CU, so the larger tile costs no parallelism.
+  if (variant == 4 && ((M + 255) / 256) * ((N + 127) / 128) >= 512)
     return dispatch<256, 128, 16, 16, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-  // Otherwise 128 x 128 tiles with 32-deep k slabs: half the barriers and
-  // slab loads per MAC of 16-deep ones; measured on MI355X 2% faster on the
-  // weight-gradient workload and 1-10% on the forward one, same bits (two
-  // waves per SIMD; 67.6 KB of LDS: two workgroups per CU).
+  // Otherwise (variant 1, and variant 4 on smaller outputs) 128 x 128 tiles
+  // with 32-deep k slabs: half the barriers and slab loads per MAC of
+  // 16-deep ones; measured on MI355X 2% faster on the weight-gradient
+  // workload and 1-10% on the forward one, same bits (two waves per SIMD;
+  // 67.6 KB of LDS: two workgroups per CU).
   return dispatch<128, 128, 32, 8, 8, false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
 }
 

@@ -90,13 +90,14 @@ const char* repro_strerror(int status);
 int repro_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                const float* B, int64_t ldb, float* C, int64_t ldc, void* stream);
 
-/* As repro_gemm with an explicit kernel variant: 0 is the default (VALU
- * multiply and add; 256x128 tiles when the output holds at least 512 of
- * them, else 128x128); 1 uses scalar global loads and 128x128 tiles; 2 uses
- * a 64x64 output tile; 3 forms each product fl(a*b) on the matrix cores
+/* As repro_gemm with an explicit kernel variant.  0 is the default, the
+ * kernel of variant 3.  3 forms each product fl(a*b) on the matrix cores
  * (v_mfma_f32_32x32x1_2b_f32 with K = 1 and C = -0, one product per output
  * element, nothing summed inside) and adds it into the output's chain on the
- * VALU.  All variants return the same bits; they exist to test that claim. */
+ * VALU (128x128 tiles).  4 multiplies and adds on the VALU (256x128 tiles
+ * when the output holds at least 512 of them, else 128x128); 1 does the same
+ * with scalar global loads and 128x128 tiles; 2 with 64x64 tiles.  All
+ * variants return the same bits; they exist to test that claim. */
 int repro_gemm_variant(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K, const float* A,
                        int64_t lda, const float* B, int64_t ldb, float* C, int64_t ldc, int32_t variant,
                        void* stream);

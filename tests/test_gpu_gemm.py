@@ -37,7 +37,7 @@ def test_shapes_transposes_variants(M, N, K, ta, tb):
     A, B = _stored(M, N, K, ta, tb, 0x8000 + M + 7 * N + 13 * K)
     ref = oracle.gemm(A, B, bool(ta), bool(tb))
     dA, dB = to_dev(A), to_dev(B)
-    for variant in (0, 1, 2, 3):
+    for variant in (0, 1, 2, 3, 4):
         C = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=variant)
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
@@ -50,7 +50,7 @@ def test_many_tiles_with_ragged_edges(ta, tb):
     A, B = _stored(M, N, K, ta, tb, 0x8800 + 2 * ta + tb)
     ref = oracle.gemm(A, B, bool(ta), bool(tb))
     dA, dB = to_dev(A), to_dev(B)
-    for variant in (0, 1, 2, 3):
+    for variant in (0, 1, 2, 3, 4):
         C = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=variant)
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
@@ -59,17 +59,20 @@ def test_many_tiles_with_ragged_edges(ta, tb):
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_large_output_tiles_every_word(ta, tb, K):
     # 4173 x 4141 outputs: 17 x 33 = 561 tiles of 256 x 128, enough for the
-    # default variant to take its large-output kernel, with partial tiles in
+    # VALU variant 4 to take its large-output kernel, with partial tiles in
     # M and N.  K = 80 is five whole 16-deep slabs (interior tiles take the
     # unchecked loads), K = 77 ends in a partial slab (every tile checked).
-    # Every output word against the oracle, and against the 128 x 128 kernel
-    # of variant 1.
+    # Every output word of the default (matrix-core products) and of
+    # variant 4 against the oracle, and variant 1's 128 x 128 kernel against
+    # them.
     M, N = 4173, 4141
     A, B = _stored(M, N, K, ta, tb, 0x8900 + 4 * ta + 2 * tb + (K & 1))
     ref = oracle.gemm(A, B, bool(ta), bool(tb))
     dA, dB = to_dev(A), to_dev(B)
     C0 = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=0)
     assert_bitwise(to_host(C0), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant=0")
+    C4 = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=4)
+    assert_bitwise(to_host(C4), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant=4")
     C1 = br.repro_gemm(dA, dB, bool(ta), bool(tb), variant=1)
     assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
 
@@ -77,12 +80,12 @@ def test_large_output_tiles_every_word(ta, tb, K):
 @pytest.mark.parametrize("M,N,K", [(4096, 4096, 16), (4096, 4096, 8), (4096, 4096, 1), (512, 640, 32)])
 def test_slab_count_edges(M, N, K):
     # Interior tiles with a single whole slab (K = 16 on the 256 x 128 kernel,
-    # K = 32 on the 128 x 128 one), a single partial slab (K = 8) and K = 1:
-    # every output word against the oracle, default variant and variant 1.
+    # K = 32 on the 128 x 128 ones), a single partial slab (K = 8) and K = 1:
+    # every output word against the oracle, variants 0, 1 and 4.
     A, B = _stored(M, N, K, 0, 0, 0x8A00 + K + (M & 7))
     ref = oracle.gemm(A, B)
     dA, dB = to_dev(A), to_dev(B)
-    for variant in (0, 1):
+    for variant in (0, 1, 4):
         C = br.repro_gemm(dA, dB, variant=variant)
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} variant={variant}")
 
@@ -133,7 +136,7 @@ def test_leading_dimensions_and_unaligned_views():
     assert (rest == 0).all()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_subnormal_operands_and_products(variant):
     # Subnormal inputs read as zero; products below 2^-126 flush; the chain's
     # exact subnormal sums flush.  Compared with the oracle's rule, for every
@@ -163,7 +166,7 @@ def _boundary_operands(rng, rows, cols):
     return x.astype(np.float32)
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_directed_flush_boundary_products(variant):
     # Every product a * b is within a few ulps of +-2^-126 (or a zero or
     # subnormal operand), so each step's product is decided by the flush rule:
@@ -183,7 +186,7 @@ def test_directed_flush_boundary_products(variant):
         assert (p == 0).any() and (np.abs(p) >= np.float32(2.0 ** -126)).any()
 
 
-@pytest.mark.parametrize("variant", [0, 1, 2, 3])
+@pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_overflowing_products(variant):
     # A product beyond the largest binary32 rounds to infinity of its sign and
     # stays there along the chain; the other outputs stay finite.
@@ -250,6 +253,8 @@ def test_forward_workload_full_size_sampled():
     digests = _repeat_digests(lambda: br.repro_gemm(dX, dW, out=Y), Y)
     assert digests == [first] * 10
     assert np.array_equal(to_host(Y).view(np.uint32), C.view(np.uint32))
+    # The VALU kernel (variant 4, large-output tiles) gives the same bits.
+    assert _repeat_digests(lambda: br.repro_gemm(dX, dW, out=Y, variant=4), Y, times=2) == [first] * 2
 
 
 def test_weight_gradient_workload_full_size_sampled():
@@ -272,6 +277,8 @@ def test_weight_gradient_workload_full_size_sampled():
     digests = _repeat_digests(lambda: br.repro_gemm(dX, ddY, trans_a=True, out=out), out)
     assert digests == [first] * 10
     assert np.array_equal(to_host(out).view(np.uint32), C.view(np.uint32))
+    assert _repeat_digests(lambda: br.repro_gemm(dX, ddY, trans_a=True, out=out, variant=4), out,
+                           times=2) == [first] * 2
 
 
 def test_errors():

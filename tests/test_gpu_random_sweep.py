@@ -47,7 +47,7 @@ def test_gemm_random_layouts(case):
     ref = oracle.gemm(As, Bs, ta, tb)
     ref_f = oracle.gemm(As, Bs, ta, tb, fused=True)
     what = f"M={M} N={N} K={K} ta={ta} tb={tb} pad={pad} off={off}"
-    for variant in (0, 1, 2, 3):
+    for variant in (0, 1, 2, 3, 4):
         out = _view(np.full((M, N), 7.0, np.float32), M, N, N + pad[2], off[2])
         br.repro_gemm(dA, dB, ta, tb, out=out, variant=variant)
         assert_bitwise(to_host(out), ref, f"{what} variant={variant}")

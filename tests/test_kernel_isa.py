@@ -139,26 +139,42 @@ def _loops(body: str):
 
 
 def test_interior_slab_loop_is_branch_free(asms):
-    # The VALU GEMMs with 16-byte loads run interior tiles through a slab loop
-    # with unchecked loads from a uniform base: no exec-mask branches, no
-    # register copies (a join of two compute paths in the loop once copied
-    # every accumulator on each pass), one 64-bit address add per load.
+    # The GEMMs with 16-byte loads run interior tiles through a slab loop with
+    # unchecked loads from a uniform base: no exec-mask branches, no register
+    # copies (a join of two compute paths in the loop once copied every
+    # accumulator on each pass), one 64-bit address add per load.
     asm = asms["gemm.hip"]
-    seen = 0
+    seen = Counter()
     for part in re.split(r"\n(?=_Z[^\s:]+:)", asm):
         m = re.match(r"(_Z[^\s:]+):", part)
-        if not m or not re.search(r"k_gemm(_fma)?ILi(256|128)ELi128E.*ELb1EEEv", m.group(1)):
+        if not m:
+            continue
+        name = m.group(1)
+        if re.search(r"k_gemm(_fma)?ILi(256|128)ELi128E.*ELb1EEEv", name):
+            # VALU tiles: BK steps x TM x TN multiplies (or fused steps).
+            def is_slab(c):
+                return c["v_mul_f32_e32"] + c["v_fmac_f32_e32"] + c["v_fma_f32"] >= 2048
+        elif re.search(r"k_gemm_mfma(_fma)?ILi(16|32)ELb[01]ELb[01]ELb1EEEv", name):
+            # Matrix-core tiles: two 32x32 products per k step; the unfused
+            # kernel adds each product on the VALU (2 x 32 adds per step).
+            fused = "k_gemm_mfma_fma" in name
+            bk = 32 if fused else 16
+
+            def is_slab(c, bk=bk, fused=fused):
+                return (c["v_mfma_f32_32x32x1_2b_f32"] == 2 * bk
+                        and c["v_add_f32_e32"] == (0 if fused else 64 * bk) and c["global_load_dwordx4"] >= 1)
+        else:
             continue
         loops = _loops(part.split(".Lfunc_end")[0])
-        interior = [c for c in loops if c["v_mul_f32_e32"] + c["v_fmac_f32_e32"] + c["v_fma_f32"] >= 2048
-                    and c["s_and_saveexec_b64"] == 0]
-        assert len(interior) == 1, (_short(m.group(1)), m.group(1))
+        interior = [c for c in loops if is_slab(c) and c["s_and_saveexec_b64"] == 0]
+        assert len(interior) == 1, (_short(name), name)
         c = interior[0]
-        assert c["v_mov_b32_e32"] == 0, (m.group(1), c["v_mov_b32_e32"])
+        assert c["v_mov_b32_e32"] == 0, (name, c["v_mov_b32_e32"])
         assert 1 <= c["global_load_dwordx4"] <= 8 and c["v_lshl_add_u64"] <= c["global_load_dwordx4"] + 2, (
-            m.group(1), c)
-        seen += 1
-    assert seen == 16  # k_gemm and k_gemm_fma, two tile shapes, 4 transposes each
+            name, c)
+        seen[_short(name)] += 1
+    # Two VALU tile shapes and one matrix-core shape, 4 transposes each.
+    assert seen == {"k_gemm": 8, "k_gemm_fma": 8, "k_gemm_mfma": 4, "k_gemm_mfma_fma": 4}, seen
 
 
 def test_no_kernel_uses_scratch(kernels):
