@@ -117,14 +117,14 @@ def parse():
     p.add_argument("--no-verify", action="store_true", help="skip the oracle check after timing")
     p.add_argument("--no-cpu-baseline", action="store_true")
     p.add_argument("--gemm-variants", action="store_true",
-                   help="only the forward GEMM workload, once each with repro_gemm variant 0 (the default: "
-                        "matrix-core products, VALU adds), variant 4 (VALU multiply and add) and repro_gemm_fma "
-                        "variant 0 (matrix cores), after one "
-                        "warm-up each: the run the matrix-core co-execution counters are taken on")
+                   help="only the forward and weight-gradient GEMM workloads, through repro_gemm variant 0 (the "
+                        "default: matrix-core products, VALU adds), variant 4 (VALU multiply and add) and "
+                        "repro_gemm_fma variant 0 (matrix cores), one warm-up and 5 timed calls each: the kernel "
+                        "comparison, and the run the matrix-core co-execution counters are taken on")
     p.add_argument("--valu-rates", action="store_true",
                    help="only the VALU issue-rate streams of libvalu_rates.so (single-opcode streams and the "
-                        "interleavings of full- and half-rate opcodes that the kernels contain): the measurement "
-                        "behind the ALU bounds")
+                        "interleavings of full- and half-rate opcodes that the kernels contain) and the co-issue "
+                        "of fp32 and bf16 matrix instructions with VALU adds: the measurements behind the ALU bounds")
     p.add_argument("--calibration-copy", action="store_true",
                    help="after timing, run one plain copy of 64 MiB (a one-replica fold without the average) whose "
                         "HBM counters calibrate the FETCH_SIZE / WRITE_SIZE readings of a profiling run")
@@ -531,32 +531,75 @@ def valu_rates():
             row[f"w{w}"] = {"rate": round(res[0], 4), "ghz": round(res[1], 3), "ms": round(res[2], 3)}
         log(row)
         out.append(row)
-    print(json.dumps({"valu_rates": out, "unit": "wave-instructions per SIMD per shader clock"}), flush=True)
+    # Matrix-core / VALU co-issue: one wave of each role on every SIMD, the
+    # passes sized so that each role alone runs about 1 ms.  overlap is
+    # (matrix alone + VALU alone - both) / min(alone): 1 when the two issue
+    # side by side, 0 when they take turns.
+    lib.valu_rates_coissue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    co = []
+    for kind, name, iters_m in ((0, "v_mfma_f32_32x32x1_2b_f32 (fp32)", 8000), (1, "v_mfma_f32_32x32x8_bf16", 16000)):
+        res = (ctypes.c_double * 3)()
+        rc = lib.valu_rates_coissue(kind, iters_m, 4000, res)
+        if rc != 0:
+            raise RuntimeError(f"valu_rates_coissue({kind}) returned {rc}")
+        both, m, v = res[0], res[1], res[2]
+        row = {"matrix": name, "with": "v_add_f32_e32", "ms_both": round(both, 3), "ms_matrix_alone": round(m, 3),
+               "ms_valu_alone": round(v, 3), "overlap": round((m + v - both) / min(m, v), 3)}
+        log(row)
+        co.append(row)
+    print(json.dumps({"valu_rates": out, "unit": "wave-instructions per SIMD per shader clock", "coissue": co}),
+          flush=True)
 
 
-def gemm_variants(torch, np, br, synth, dev):
-    """The forward GEMM workload through the default kernel (matrix-core
-    products, VALU adds), the VALU multiply-and-add kernel, and the fused
-    matrix-core kernel."""
-    GC = synth.GEMM
-    X = torch.from_numpy(synth.gemm_x()).to(dev).view(GC["M"], GC["K"])
-    W = torch.from_numpy(synth.gemm_w()).to(dev).view(GC["K"], GC["N"])
-    Y = torch.empty(GC["M"], GC["N"], dtype=torch.float32, device=dev)
-    runs = {"repro_gemm_variant0": lambda: br.repro_gemm(X, W, out=Y, variant=0),
-            "repro_gemm_variant4": lambda: br.repro_gemm(X, W, out=Y, variant=4),
-            "repro_gemm_fma_variant0": lambda: br.repro_gemm_fma(X, W, out=Y, variant=0)}
+def gemm_variants(torch, np, br, synth, dev, reps=5):
+    """The forward and weight-gradient GEMM workloads through the default
+    kernel (matrix-core products, VALU adds), the VALU multiply-and-add
+    kernel, and the fused matrix-core kernel: one warm-up call, then `reps`
+    calls timed one by one with events (median and min).  The unfused
+    variants must give the same digest."""
+    up = Upload(torch)
+    GC, DC = synth.GEMM, synth.DW
+    X3 = torch.empty(GC["M"] * GC["K"], dtype=torch.float32, device=dev)
+    W3 = torch.empty(GC["K"] * GC["N"], dtype=torch.float32, device=dev)
+    up.fill(X3, lambda m, offset, out: synth.generate(m, synth.NORMAL, synth.tid(3, 0), 1.0, offset=offset, out=out),
+            X3.numel())
+    up.fill(W3, lambda m, offset, out: synth.generate(m, synth.NORMAL, synth.tid(3, 1), 0.02, offset=offset,
+                                                      out=out), W3.numel())
+    X5 = torch.empty(DC["K"] * DC["M"], dtype=torch.float32, device=dev)
+    dY5 = torch.empty(DC["K"] * DC["N"], dtype=torch.float32, device=dev)
+    up.fill(X5, lambda m, offset, out: synth.generate(m, synth.STUDENT_T3, synth.tid(5, 0), 1e-2, offset=offset,
+                                                      out=out), X5.numel())
+    up.fill(dY5, lambda m, offset, out: synth.generate(m, synth.STUDENT_T3, synth.tid(5, 1), 1e-2, offset=offset,
+                                                       out=out), dY5.numel())
+    X3, W3 = X3.view(GC["M"], GC["K"]), W3.view(GC["K"], GC["N"])
+    X5, dY5 = X5.view(DC["K"], DC["M"]), dY5.view(DC["K"], DC["N"])
+    Y = torch.empty(max(GC["M"] * GC["N"], DC["M"] * DC["N"]), dtype=torch.float32, device=dev)
+    Y3, Y5 = Y[:GC["M"] * GC["N"]].view(GC["M"], GC["N"]), Y[:DC["M"] * DC["N"]].view(DC["M"], DC["N"])
+    shapes = {"fwd": (lambda f, v: f(X3, W3, out=Y3, variant=v), Y3, 2.0 * GC["M"] * GC["N"] * GC["K"]),
+              "dw": (lambda f, v: f(X5, dY5, trans_a=True, out=Y5, variant=v), Y5, 2.0 * DC["M"] * DC["N"] * DC["K"])}
+    kernels = {"repro_gemm_variant0": (br.repro_gemm, 0), "repro_gemm_variant4": (br.repro_gemm, 4),
+               "repro_gemm_fma_variant0": (br.repro_gemm_fma, 0)}
     out = {}
-    for name, call in runs.items():
-        call()
-        e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-        e0.record()
-        call()
-        e1.record()
-        torch.cuda.synchronize()
-        out[name] = {"ms": round(e0.elapsed_time(e1), 4),
-                     "digest": br.repro_state_hash(Y.view(-1)).hex()}
-        log(name, out[name])
-    print(json.dumps({"gemm_variants": out, "workload": "gemm 8192x2048 @ 2048x8192"}), flush=True)
+    for shape, (call, Yv, flops) in shapes.items():
+        for name, (f, v) in kernels.items():
+            call(f, v)
+            ts = []
+            for _ in range(reps):
+                e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+                e0.record()
+                call(f, v)
+                e1.record()
+                torch.cuda.synchronize()
+                ts.append(e0.elapsed_time(e1))
+            med = float(np.median(ts))
+            out[f"{shape}_{name}"] = {"ms_median": round(med, 4), "ms_min": round(min(ts), 4),
+                                      "tflops": round(flops / med / 1e9, 2),
+                                      "digest": br.repro_state_hash(Yv.reshape(-1)).hex()}
+            log(shape, name, out[f"{shape}_{name}"])
+        if out[f"{shape}_repro_gemm_variant0"]["digest"] != out[f"{shape}_repro_gemm_variant4"]["digest"]:
+            raise RuntimeError(f"{shape}: the unfused variants gave different bits")
+    print(json.dumps({"gemm_variants": out, "workloads": {"fwd": "8192x2048 @ 2048x8192",
+                                                          "dw": "(16384x2048)^T @ 16384x8192"}}), flush=True)
 
 
 def verify(torch, np, br, reps, g_red, X3, W3, Y3, X5, dY5, dW5, state, ws, n, aidx, samples, hp, step0, nsteps):

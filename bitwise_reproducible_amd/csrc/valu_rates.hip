@@ -1,6 +1,7 @@
 // Measurement support for the ALU rooflines (not part of the reproducible
 // operations): the VALU issue rate of gfx950 for single-instruction streams
-// and for the interleavings that the kernels' instruction mixes contain.
+// and for the interleavings that the kernels' instruction mixes contain, and
+// whether matrix-core instructions issue alongside VALU work on one SIMD.
 //
 // Each stream is 128 independent instructions (sources v0..v15, results
 // v16..v47, no dependences between them) repeated in a loop; a workgroup of
@@ -106,6 +107,68 @@ __global__ __launch_bounds__(256) void k_valu_stream(float* __restrict__ out, lo
   }
 }
 
+// Co-issue of matrix-core instructions with VALU adds on one SIMD.  A
+// 512-lane workgroup has 8 waves and wave w runs on SIMD w % 4, so waves 0-3
+// (matrix role) and waves 4-7 (VALU role) pair up, one of each per SIMD.
+// The matrix role runs 4 independent accumulating chains (fp32
+// v_mfma_f32_32x32x1_2b_f32, or bf16 v_mfma_f32_32x32x8_bf16); the VALU role
+// runs the v_add_f32 stream.  MODE 0 runs both roles, 1 only the matrix role,
+// 2 only the VALU role (the other waves exit at once).
+typedef float v32f __attribute__((ext_vector_type(32)));
+typedef float v16f __attribute__((ext_vector_type(16)));
+typedef short v4s __attribute__((ext_vector_type(4)));
+#define ADD8 \
+  "v_add_f32_e32 v16, v0, v1\n" "v_add_f32_e32 v17, v2, v3\n" "v_add_f32_e32 v18, v4, v5\n" \
+  "v_add_f32_e32 v19, v6, v7\n" "v_add_f32_e32 v20, v8, v9\n" "v_add_f32_e32 v21, v10, v11\n" \
+  "v_add_f32_e32 v22, v12, v13\n" "v_add_f32_e32 v23, v14, v15\n"
+
+template <int KIND, int MODE>
+__global__ __launch_bounds__(512) void k_coissue(float* __restrict__ out, int iters_m, int iters_v) {
+  const int wave = threadIdx.x >> 6;
+  const int lane = threadIdx.x & 63;
+  float r = 0.0f;
+  if (wave < 4) {
+    if (MODE == 2) return;
+    if constexpr (KIND == 0) {
+      const float a = 1.0f + lane, b = 0.5f - lane;
+      v32f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+      for (int it = 0; it < iters_m; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x1f32(b, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x1f32(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x1f32(b, b, c3, 0, 0, 0);
+      }
+      for (int i = 0; i < 32; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+    } else {
+      const v4s a = {(short)lane, 0x3f80, 0x3f00, 0x4000}, b = {0x3f80, (short)lane, 0x3e80, 0x3f80};
+      v16f c0 = {}, c1 = {}, c2 = {}, c3 = {};
+      for (int it = 0; it < iters_m; ++it) {
+        c0 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, b, c0, 0, 0, 0);
+        c1 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(b, a, c1, 0, 0, 0);
+        c2 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(a, a, c2, 0, 0, 0);
+        c3 = __builtin_amdgcn_mfma_f32_32x32x8bf16_1k(b, b, c3, 0, 0, 0);
+      }
+      for (int i = 0; i < 16; ++i) r += c0[i] + c1[i] + c2[i] + c3[i];
+    }
+  } else {
+    if (MODE == 1) return;
+    asm volatile(
+        "v_cvt_f32_u32 v0, 1\n v_cvt_f32_u32 v1, 2\n v_cvt_f32_u32 v2, 3\n v_cvt_f32_u32 v3, 5\n"
+        "v_cvt_f32_u32 v4, 7\n v_cvt_f32_u32 v5, 11\n v_cvt_f32_u32 v6, 13\n v_cvt_f32_u32 v7, 17\n"
+        "v_cvt_f32_u32 v8, 19\n v_cvt_f32_u32 v9, 23\n v_cvt_f32_u32 v10, 29\n v_cvt_f32_u32 v11, 31\n"
+        "v_cvt_f32_u32 v12, 37\n v_cvt_f32_u32 v13, 41\n v_cvt_f32_u32 v14, 43\n v_cvt_f32_u32 v15, 47\n" ::
+            : "v0", "v1", "v2", "v3", "v4", "v5", "v6", "v7", "v8", "v9", "v10", "v11", "v12", "v13", "v14", "v15");
+    for (int it = 0; it < iters_v; ++it)
+      asm volatile(R8(ADD8) R8(ADD8)::: "v16", "v17", "v18", "v19", "v20", "v21", "v22", "v23");
+    asm volatile("v_mov_b32 %0, v16" : "=v"(r)::"v16");
+  }
+  out[(size_t)blockIdx.x * 512 + threadIdx.x] = r;
+}
+
+typedef void (*CoissueKernel)(float*, int, int);
+constexpr CoissueKernel kCoissue[2][3] = {{k_coissue<0, 0>, k_coissue<0, 1>, k_coissue<0, 2>},
+                                          {k_coissue<1, 0>, k_coissue<1, 1>, k_coissue<1, 2>}};
+
 typedef void (*StreamKernel)(float*, long long*, int);
 constexpr StreamKernel kKernels[kStreams] = {k_valu_stream<0>, k_valu_stream<1>, k_valu_stream<2>, k_valu_stream<3>,
                                              k_valu_stream<4>, k_valu_stream<5>, k_valu_stream<6>, k_valu_stream<7>,
@@ -175,6 +238,40 @@ int valu_rates_run(int s, int waves_per_simd, int iters, double* result) {
   if (e1) (void)hipEventDestroy(e1);
   if (out) (void)hipFree(out);
   if (meta) (void)hipFree(meta);
+  return rc;
+}
+
+// Event milliseconds of the co-issue kernel for matrix kind `kind` (0 fp32,
+// 1 bf16) in each mode: result[0] both roles, [1] the matrix role alone,
+// [2] the VALU role alone.  One 512-lane workgroup per CU; the matrix role
+// runs `iters_m` passes of 4 instructions, the VALU role `iters_v` passes of
+// 128 adds.  Returns 0, or -1 for bad arguments, -2 for a HIP error.
+int valu_rates_coissue(int kind, int iters_m, int iters_v, double* result) {
+  if (kind < 0 || kind > 1 || iters_m < 1 || iters_v < 1 || result == nullptr) return -1;
+  int dev = 0, cus = 0;
+  if (hipGetDevice(&dev) != hipSuccess ||
+      hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || cus < 1)
+    return -2;
+  float* out = nullptr;
+  hipEvent_t e0 = nullptr, e1 = nullptr;
+  int rc = -2;
+  if (hipMalloc(&out, sizeof(float) * 512 * (size_t)cus) == hipSuccess && hipEventCreate(&e0) == hipSuccess &&
+      hipEventCreate(&e1) == hipSuccess) {
+    rc = 0;
+    for (int mode = 0; mode < 3 && rc == 0; ++mode) {
+      hipLaunchKernelGGL(kCoissue[kind][mode], dim3(cus), dim3(512), 0, 0, out, 16, 16);
+      (void)hipEventRecord(e0, 0);
+      hipLaunchKernelGGL(kCoissue[kind][mode], dim3(cus), dim3(512), 0, 0, out, iters_m, iters_v);
+      (void)hipEventRecord(e1, 0);
+      float ms = 0.f;
+      if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f)
+        rc = -2;
+      result[mode] = ms;
+    }
+  }
+  if (e0) (void)hipEventDestroy(e0);
+  if (e1) (void)hipEventDestroy(e1);
+  if (out) (void)hipFree(out);
   return rc;
 }
 

@@ -118,8 +118,8 @@ def _product_sets(seed, n):
 def test_step_with_negative_zero_is_the_product(unit):
     # With C = -0 (the identity of IEEE addition, which keeps a zero
     # product's sign) a single step is the bare product fl(a * b) under the
-    # contract, bit for bit, on every unit.  The unfused GEMM's variant 3 takes
-    # its products from v_mfma_f32_32x32x1_2b_f32 (unit 1) this way.
+    # contract, bit for bit, on every unit.  The unfused GEMM's default kernel
+    # takes its products from v_mfma_f32_32x32x1_2b_f32 (unit 1) this way.
     for name, (a, b) in _product_sets(300 + unit, 100_003).items():
         ref = oracle.fp32_op(oracle.OP_MUL, a, b)
         if name == "overflow":

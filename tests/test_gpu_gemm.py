@@ -140,7 +140,7 @@ def test_leading_dimensions_and_unaligned_views():
 def test_subnormal_operands_and_products(variant):
     # Subnormal inputs read as zero; products below 2^-126 flush; the chain's
     # exact subnormal sums flush.  Compared with the oracle's rule, for every
-    # variant (variant 3 forms the products on the matrix cores).
+    # variant (variants 0 and 3 form the products on the matrix cores).
     rng = np.random.default_rng(5)
     M, N, K = 32, 32, 40
     A = (rng.standard_normal((M, K)) * 2.0 ** -63).astype(np.float32)
