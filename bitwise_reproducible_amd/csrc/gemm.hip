@@ -571,9 +571,9 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   if (fused) {  // variant 0: matrix cores, 1: VALU v_fma_f32
     if (variant == 0)
       return dispatch_mfma<true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
-    // The same tiles as the unfused default: 256 x 128 for large outputs
-    // (measured 4-5% faster than 128 x 128 on both workloads), else
-    // 128 x 128 with 32-deep slabs.
+    // The same tiles as the unfused VALU kernel (variant 4): 256 x 128 for
+    // large outputs (measured 4-5% faster than 128 x 128 on both
+    // workloads), else 128 x 128 with 32-deep slabs.
     if (((M + 255) / 256) * ((N + 127) / 128) >= 512)
       return dispatch<256, 128, 16, 16, 8, true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
     return dispatch<128, 128, 32, 8, 8, true>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
@@ -582,8 +582,8 @@ hipError_t launch_gemm(int trans_a, int trans_b, int64_t M, int64_t N, int64_t K
   // adds on the VALU (k_gemm_mfma).  The matrix cores and the VALU take
   // turns on this chip, so per MAC this costs what the VALU's multiply and
   // add cost; but with half the VALU instructions the kernel runs at a
-  // higher clock, and measured on MI355X it is 0-10% faster than the VALU
-  // kernel on both GEMM workloads, with the same bits.
+  // higher clock, and measured on MI355X it is 1-6% faster than the VALU
+  // kernel on the two GEMM workloads, with the same bits.
   if (variant == 0 || variant == 3)
     return dispatch_mfma<false>(trans_a, trans_b, vec, M, N, K, A, lda, B, ldb, C, ldc, stream);
   if (variant == 2)
