@@ -3,8 +3,8 @@
 // and for the interleavings that the kernels' instruction mixes contain, and
 // whether matrix-core instructions issue alongside VALU work on one SIMD.
 //
-// Each stream is 128 independent instructions (sources v0..v15, results
-// v16..v47, no dependences between them) repeated in a loop; a workgroup of
+// Each stream is a loop body of 128 to 260 independent instructions
+// (sources v0..v15, results v16..v47, no dependences between them); a workgroup of
 // 256 lanes puts one wave on each SIMD of its CU, and a launch of
 // 256 x W workgroups puts W waves on every SIMD.  The rate is wave-
 // instructions per SIMD per shader clock over the launch's event time, with
@@ -53,10 +53,25 @@ namespace {
   "v_xor_b32_e32 v19, v6, v7\n" "v_alignbit_b32 v28, v8, v9, 24\n" "v_xor_b32_e32 v21, v10, v11\n" \
   "v_alignbit_b32 v30, v12, v13, 24\n" "v_xor_b32_e32 v23, v14, v15\n"
 #define ONE_IN_65 R8(XOR8) "v_alignbit_b32 v24, v0, v1, 24\n"
+#define ALIGN4 \
+  "v_alignbit_b32 v24, v0, v1, 24\n" "v_alignbit_b32 v25, v2, v3, 24\n" "v_alignbit_b32 v26, v4, v5, 24\n" \
+  "v_alignbit_b32 v27, v6, v7, 24\n"
+#define XOR4 \
+  "v_xor_b32_e32 v16, v0, v1\n" "v_xor_b32_e32 v17, v2, v3\n" "v_xor_b32_e32 v18, v4, v5\n" \
+  "v_xor_b32_e32 v19, v6, v7\n"
+// The G function's mix: 6 64-bit adds and 6 alignbits (half-rate) beside
+// 8 xors (full-rate), clustered by kind.
+#define G_MIX \
+  "v_lshl_add_u64 v[32:33], v[0:1], 0, v[2:3]\n" "v_lshl_add_u64 v[34:35], v[4:5], 0, v[6:7]\n" \
+  "v_lshl_add_u64 v[36:37], v[8:9], 0, v[10:11]\n" "v_lshl_add_u64 v[38:39], v[12:13], 0, v[14:15]\n" \
+  "v_lshl_add_u64 v[40:41], v[2:3], 0, v[4:5]\n" "v_lshl_add_u64 v[42:43], v[6:7], 0, v[8:9]\n" \
+  "v_alignbit_b32 v24, v0, v1, 24\n" "v_alignbit_b32 v25, v2, v3, 24\n" "v_alignbit_b32 v26, v4, v5, 24\n" \
+  "v_alignbit_b32 v27, v6, v7, 24\n" "v_alignbit_b32 v28, v8, v9, 24\n" "v_alignbit_b32 v29, v10, v11, 24\n" \
+  XOR8
 
-constexpr int kStreams = 10;
+constexpr int kStreams = 14;
 // Instructions per pass of each stream's loop body.
-constexpr int kPassLength[kStreams] = {128, 128, 128, 128, 128, 128, 128, 128, 260, 130};
+constexpr int kPassLength[kStreams] = {128, 128, 128, 128, 128, 128, 128, 128, 260, 130, 128, 128, 128, 160};
 
 #define CLOBBERS                                                                                              \
   "v16", "v17", "v18", "v19", "v20", "v21", "v22", "v23", "v24", "v25", "v26", "v27", "v28", "v29", "v30", \
@@ -80,6 +95,15 @@ __device__ __forceinline__ void pass() {
                                      "v_alignbit_b32 v27, v6, v7, 24\n" ::: CLOBBERS);
   // One v_alignbit_b32 per 65 instructions.
   if constexpr (S == 9) asm volatile(ONE_IN_65 ONE_IN_65 ::: CLOBBERS);
+  // Long runs of each kind: 64 v_alignbit_b32, then 64 v_xor_b32.
+  if constexpr (S == 10) asm volatile(R8(ALIGN8) R8(XOR8) ::: CLOBBERS);
+  // One half-rate instruction in four, clustered: 4 v_alignbit_b32, 12 v_xor_b32.
+  if constexpr (S == 11) asm volatile(R8(ALIGN4 XOR4 XOR4 XOR4) ::: CLOBBERS);
+  // 8 v_lshl_add_u64, then 8 v_xor_b32.
+  if constexpr (S == 12) asm volatile(ADD64_8 XOR8 ADD64_8 XOR8 ADD64_8 XOR8 ADD64_8 XOR8 ADD64_8 XOR8 ADD64_8 XOR8
+                                          ADD64_8 XOR8 ADD64_8 XOR8 ::: CLOBBERS);
+  // The G function's mix, clustered by kind (20 instructions, 12 half-rate).
+  if constexpr (S == 13) asm volatile(R8(G_MIX) ::: CLOBBERS);
 }
 
 template <int S>
@@ -170,9 +194,10 @@ constexpr CoissueKernel kCoissue[2][3] = {{k_coissue<0, 0>, k_coissue<0, 1>, k_c
                                           {k_coissue<1, 0>, k_coissue<1, 1>, k_coissue<1, 2>}};
 
 typedef void (*StreamKernel)(float*, long long*, int);
-constexpr StreamKernel kKernels[kStreams] = {k_valu_stream<0>, k_valu_stream<1>, k_valu_stream<2>, k_valu_stream<3>,
-                                             k_valu_stream<4>, k_valu_stream<5>, k_valu_stream<6>, k_valu_stream<7>,
-                                             k_valu_stream<8>, k_valu_stream<9>};
+constexpr StreamKernel kKernels[kStreams] = {k_valu_stream<0>,  k_valu_stream<1>,  k_valu_stream<2>,  k_valu_stream<3>,
+                                             k_valu_stream<4>,  k_valu_stream<5>,  k_valu_stream<6>,  k_valu_stream<7>,
+                                             k_valu_stream<8>,  k_valu_stream<9>,  k_valu_stream<10>, k_valu_stream<11>,
+                                             k_valu_stream<12>, k_valu_stream<13>};
 
 }  // namespace
 
@@ -190,7 +215,11 @@ const char* valu_rates_name(int s) {
                                               "v_lshrrev_b32_e32",
                                               "v_alignbit_b32 and v_xor_b32_e32 alternating",
                                               "4 v_alignbit_b32 after 256 v_xor_b32_e32",
-                                              "1 v_alignbit_b32 per 65 instructions"};
+                                              "1 v_alignbit_b32 per 65 instructions",
+                                              "64 v_alignbit_b32 then 64 v_xor_b32_e32",
+                                              "4 v_alignbit_b32 then 12 v_xor_b32_e32",
+                                              "8 v_lshl_add_u64 then 8 v_xor_b32_e32",
+                                              "G mix: 6 v_lshl_add_u64, 6 v_alignbit_b32, 8 v_xor_b32_e32"};
   return s >= 0 && s < kStreams ? names[s] : nullptr;
 }
 
