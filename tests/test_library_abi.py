@@ -92,3 +92,25 @@ def test_product_path_has_no_oracle_or_fallback():
                 assert "import oracle" not in text and "from oracle" not in text, f
                 assert "repro_oracle" not in text, f
     assert "oracle" not in sys.modules["bitwise_reproducible_amd"].__dict__
+
+
+def test_issue_rate_library_exports_its_streams():
+    # The measurement library behind the ALU bounds (bench.py --valu-rates):
+    # its stream table and entry points load without a GPU.
+    path = os.path.join(ROOT, "bitwise_reproducible_amd", "libvalu_rates.so")
+    lib = ctypes.CDLL(path)
+    for name in ("valu_rates_count", "valu_rates_name", "valu_rates_run", "valu_rates_coissue"):
+        assert hasattr(lib, name), name
+    lib.valu_rates_name.restype = ctypes.c_char_p
+    count = lib.valu_rates_count()
+    names = [lib.valu_rates_name(s).decode() for s in range(count)]
+    assert count == 14 and len(set(names)) == count
+    assert lib.valu_rates_name(count) is None and lib.valu_rates_name(-1) is None
+    # Argument checks return before any device call.
+    res = (ctypes.c_double * 3)()
+    lib.valu_rates_run.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    lib.valu_rates_coissue.argtypes = [ctypes.c_int, ctypes.c_int, ctypes.c_int, ctypes.POINTER(ctypes.c_double)]
+    assert lib.valu_rates_run(count, 2, 10, res) == -1
+    assert lib.valu_rates_run(0, 9, 10, res) == -1
+    assert lib.valu_rates_coissue(2, 10, 10, res) == -1
+    assert lib.valu_rates_coissue(0, 0, 10, res) == -1
