@@ -500,15 +500,16 @@ hipError_t launch_mfma(int64_t M, int64_t N, int64_t K, const float* A, int64_t 
   return hipGetLastError();
 }
 
-// The fused chains take 32-deep k slabs (half the barriers; 4-5% faster
-// measured), the products-plus-VALU-adds variant 16-deep ones.
+// 32-deep k slabs: half the barriers and slab loads per MAC of 16-deep
+// ones; measured on MI355X 4-5% faster for the fused chains and 1% for the
+// products-plus-VALU-adds kernel (220 VGPRs: still two waves per SIMD).
 template <bool FUSED>
 hipError_t dispatch_mfma(int ta, int tb, bool vec, int64_t M, int64_t N, int64_t K, const float* A, int64_t lda,
                          const float* B, int64_t ldb, float* C, int64_t ldc, hipStream_t stream) {
 #define REPRO_GEMM_CASE(TA_, TB_)                                                                     \
   if (ta == TA_ && tb == TB_)                                                                         \
-    return vec ? launch_mfma<(FUSED ? 32 : 16), TA_, TB_, true, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream) \
-               : launch_mfma<(FUSED ? 32 : 16), TA_, TB_, false, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream);
+    return vec ? launch_mfma<32, TA_, TB_, true, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream) \
+               : launch_mfma<32, TA_, TB_, false, FUSED>(M, N, K, A, lda, B, ldb, C, ldc, stream);
   REPRO_GEMM_CASE(0, 0)
   REPRO_GEMM_CASE(1, 0)
   REPRO_GEMM_CASE(0, 1)

@@ -174,13 +174,14 @@ def test_fused_several_tiles_with_ragged_edges(ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} fused variant={variant}")
 
 
-@pytest.mark.parametrize("K", [80, 77])
+@pytest.mark.parametrize("K", [96, 77])
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_fused_large_output_tiles_every_word(ta, tb, K):
     # 4173 x 4141 outputs (561 tiles of 256 x 128, partial in M and N): the
-    # VALU variant takes its large-output kernel, with whole 16-deep slabs
-    # (K = 80) or a partial last one (K = 77).  Every word against the
-    # oracle's fused chains, and the matrix-core variant against it.
+    # VALU variant takes its large-output kernel.  K = 96 is whole slabs for
+    # both kernels (six 16-deep on the VALU, three 32-deep on the matrix
+    # cores), K = 77 ends in a partial one.  Every word against the oracle's
+    # fused chains, and the matrix-core variant against it.
     M, N = 4173, 4141
     tid = 0x9900 + 4 * ta + 2 * tb + (K & 1)
     A = _mat(K, M, tid) if ta else _mat(M, K, tid)

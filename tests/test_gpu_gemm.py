@@ -55,13 +55,14 @@ def test_many_tiles_with_ragged_edges(ta, tb):
         assert_bitwise(to_host(C), ref, f"{M}x{N}x{K} ta={ta} tb={tb} variant={variant}")
 
 
-@pytest.mark.parametrize("K", [80, 77])
+@pytest.mark.parametrize("K", [96, 77])
 @pytest.mark.parametrize("ta,tb", [(0, 0), (1, 0), (0, 1), (1, 1)])
 def test_large_output_tiles_every_word(ta, tb, K):
     # 4173 x 4141 outputs: 17 x 33 = 561 tiles of 256 x 128, enough for the
     # VALU variant 4 to take its large-output kernel, with partial tiles in
-    # M and N.  K = 80 is five whole 16-deep slabs (interior tiles take the
-    # unchecked loads), K = 77 ends in a partial slab (every tile checked).
+    # M and N.  K = 96 is three whole 32-deep slabs of the default kernel and
+    # six 16-deep ones of variant 4 (interior tiles take the unchecked
+    # loads), K = 77 ends in a partial slab (every tile checked).
     # Every output word of the default (matrix-core products) and of
     # variant 4 against the oracle, and variant 1's 128 x 128 kernel against
     # them.
@@ -77,11 +78,13 @@ def test_large_output_tiles_every_word(ta, tb, K):
     assert torch.equal(C0.view(torch.int32), C1.view(torch.int32))
 
 
-@pytest.mark.parametrize("M,N,K", [(4096, 4096, 16), (4096, 4096, 8), (4096, 4096, 1), (512, 640, 32)])
+@pytest.mark.parametrize("M,N,K", [(4096, 4096, 16), (4096, 4096, 8), (4096, 4096, 1), (512, 640, 32),
+                                   (1024, 1024, 64), (1024, 1024, 48)])
 def test_slab_count_edges(M, N, K):
-    # Interior tiles with a single whole slab (K = 16 on the 256 x 128 kernel,
-    # K = 32 on the 128 x 128 ones), a single partial slab (K = 8) and K = 1:
-    # every output word against the oracle, variants 0, 1 and 4.
+    # Interior tiles with one or two whole slabs (K = 16 on the VALU kernel's
+    # 256 x 128 tiles, K = 32 and 64 on the 128 x 128 ones, 32-deep), a whole
+    # slab and a partial one (K = 48), a single partial slab (K = 8 or 16)
+    # and K = 1: every output word against the oracle, variants 0, 1 and 4.
     A, B = _stored(M, N, K, 0, 0, 0x8A00 + K + (M & 7))
     ref = oracle.gemm(A, B)
     dA, dB = to_dev(A), to_dev(B)

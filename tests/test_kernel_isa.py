@@ -154,11 +154,12 @@ def test_interior_slab_loop_is_branch_free(asms):
             # VALU tiles: BK steps x TM x TN multiplies (or fused steps).
             def is_slab(c):
                 return c["v_mul_f32_e32"] + c["v_fmac_f32_e32"] + c["v_fma_f32"] >= 2048
-        elif re.search(r"k_gemm_mfma(_fma)?ILi(16|32)ELb[01]ELb[01]ELb1EEEv", name):
-            # Matrix-core tiles: two 32x32 products per k step; the unfused
-            # kernel adds each product on the VALU (2 x 32 adds per step).
+        elif re.search(r"k_gemm_mfma(_fma)?ILi32ELb[01]ELb[01]ELb1EEEv", name):
+            # Matrix-core tiles, 32-deep slabs: two 32x32 products per k step;
+            # the unfused kernel adds each product on the VALU (2 x 32 adds
+            # per step).
             fused = "k_gemm_mfma_fma" in name
-            bk = 32 if fused else 16
+            bk = 32
 
             def is_slab(c, bk=bk, fused=fused):
                 return (c["v_mfma_f32_32x32x1_2b_f32"] == 2 * bk
