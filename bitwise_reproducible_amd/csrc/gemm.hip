@@ -8,10 +8,15 @@
 //
 // Design for gfx950:
 //  - gfx950 has no unfused multiply-add instruction, and fused ones round
-//    once, so every step is a v_mul_f32 followed by a v_add_f32.  The file
-//    is built with -ffp-contract=off and without packed-fp32 instructions;
-//    the instruction-mix audit in the tests checks that no v_fma / v_fmac /
-//    v_pk_* appears in the unfused kernels.
+//    once, so every step is a rounded product and a v_add_f32.  The default
+//    kernel (k_gemm_mfma) forms the products on the matrix cores:
+//    v_mfma_f32_32x32x1_2b_f32 with K = 1 and C = -0 returns fl(a * b) for
+//    2,048 pairs at once.  The VALU kernel (k_gemm) uses v_mul_f32.  The
+//    matrix cores and the VALU take turns on a SIMD and the products cost
+//    the same SIMD time either way; the matrix-core form holds a higher
+//    clock.  The file is built with -ffp-contract=off and without
+//    packed-fp32 instructions; the instruction-mix audit in the tests checks
+//    that no v_fma / v_fmac / v_pk_* appears in the unfused kernels.
 //  - repro_gemm_fma declares the other convention (one fused step per k);
 //    its kernels, k_gemm_fma (v_fma_f32) and k_gemm_mfma_fma (matrix cores),
 //    share the tiling below and differ only in the step.
@@ -21,13 +26,16 @@
 //    this flush is the x86 FTZ/DAZ rule bit for bit; repro_fp32_ops exposes
 //    the same v_mul_f32 / v_add_f32 for the directed boundary tests).
 //  - Work is split over output tiles only.  A workgroup of 256 lanes owns a
-//    BM x BN tile; each lane owns a TM x TN register tile and walks the
-//    K dimension in ascending BK-wide slabs staged through LDS (double
-//    buffered, one barrier per slab), so every output keeps a single serial
-//    chain in its own register.  No split-k, no atomics, no cross-lane sums.
+//    BM x BN tile and walks the K dimension in ascending BK-wide slabs
+//    staged through LDS (double buffered, one barrier per slab); each lane
+//    (VALU kernel: a TM x TN register tile) or each wave (matrix cores: a
+//    64 x 64 tile held in the instructions' output registers) keeps every
+//    output's single serial chain in its own register.  No split-k, no
+//    atomics, no cross-lane sums.
 //  - A and B slabs are loaded with 16-byte global loads when the layout
-//    allows and transposed into k-major LDS rows, so that the inner loop
-//    reads a and b fragments as 16-byte LDS vectors.
+//    allows and stored k-major in LDS, so that the inner loop reads a and b
+//    fragments (VALU: 16-byte vectors) or matrix operands (one word per
+//    lane) with no bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
