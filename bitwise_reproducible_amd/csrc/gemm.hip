@@ -35,7 +35,7 @@
 //  - A and B slabs are loaded with 16-byte global loads when the layout
 //    allows and stored k-major in LDS, so that the inner loop reads a and b
 //    fragments (VALU: 16-byte vectors) or matrix operands (one word per
-//    lane) with no bank conflicts.
+//    lane) with few bank conflicts.
 #include <hip/hip_runtime.h>
 
 #include <type_traits>
