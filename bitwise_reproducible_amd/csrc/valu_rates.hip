@@ -243,12 +243,15 @@ int valu_rates_run(int s, int waves_per_simd, int iters, double* result) {
       hipMalloc(&meta, sizeof(long long) * 8 * (size_t)blocks) == hipSuccess && hipEventCreate(&e0) == hipSuccess &&
       hipEventCreate(&e1) == hipSuccess) {
     hipLaunchKernelGGL(kKernels[s], dim3(blocks), dim3(256), 0, 0, out, meta, 16);
+    const hipError_t warm = hipGetLastError();
     (void)hipEventRecord(e0, 0);
     hipLaunchKernelGGL(kKernels[s], dim3(blocks), dim3(256), 0, 0, out, meta, iters);
+    const hipError_t timed = hipGetLastError();
     (void)hipEventRecord(e1, 0);
     float ms = 0.f;
     std::vector<long long> h(8 * (size_t)blocks);
-    if (hipEventSynchronize(e1) == hipSuccess && hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
+    if (warm == hipSuccess && timed == hipSuccess && hipEventSynchronize(e1) == hipSuccess &&
+        hipEventElapsedTime(&ms, e0, e1) == hipSuccess &&
         hipMemcpy(h.data(), meta, sizeof(long long) * h.size(), hipMemcpyDeviceToHost) == hipSuccess && ms > 0.f) {
       double cyc = 0, rt = 0;
       for (size_t w = 0; w < 4 * (size_t)blocks; ++w) {
@@ -289,11 +292,14 @@ int valu_rates_coissue(int kind, int iters_m, int iters_v, double* result) {
     rc = 0;
     for (int mode = 0; mode < 3 && rc == 0; ++mode) {
       hipLaunchKernelGGL(kCoissue[kind][mode], dim3(cus), dim3(512), 0, 0, out, 16, 16);
+      const hipError_t warm = hipGetLastError();
       (void)hipEventRecord(e0, 0);
       hipLaunchKernelGGL(kCoissue[kind][mode], dim3(cus), dim3(512), 0, 0, out, iters_m, iters_v);
+      const hipError_t timed = hipGetLastError();
       (void)hipEventRecord(e1, 0);
       float ms = 0.f;
-      if (hipEventSynchronize(e1) != hipSuccess || hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f)
+      if (warm != hipSuccess || timed != hipSuccess || hipEventSynchronize(e1) != hipSuccess ||
+          hipEventElapsedTime(&ms, e0, e1) != hipSuccess || ms <= 0.f)
         rc = -2;
       result[mode] = ms;
     }
