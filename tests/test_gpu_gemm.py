@@ -176,9 +176,10 @@ def test_directed_flush_boundary_products(variant):
     # tiny after rounding -> signed zero, otherwise the rounded product.  The
     # chain then adds values of a few times 2^-126, whose exact sums are normal
     # or flush.  One GEMM per variant against the oracle, plus the K = 1 case
-    # where every output is a single product.
+    # where every output is a single product; 256 x 256 x 64 has 16-byte rows
+    # and whole slabs, so its tiles take the unchecked interior loop.
     rng = np.random.default_rng(11)
-    for M, N, K in ((64, 64, 1), (96, 80, 37), (130, 129, 64)):
+    for M, N, K in ((64, 64, 1), (96, 80, 37), (130, 129, 64), (256, 256, 64)):
         A = _boundary_operands(rng, M, K)
         B = _boundary_operands(rng, K, N)
         ref = oracle.gemm(A, B)
@@ -192,8 +193,13 @@ def test_directed_flush_boundary_products(variant):
 @pytest.mark.parametrize("variant", [0, 1, 2, 3, 4])
 def test_overflowing_products(variant):
     # A product beyond the largest binary32 rounds to infinity of its sign and
-    # stays there along the chain; the other outputs stay finite.
-    M, N, K = 70, 66, 33
+    # stays there along the chain; the other outputs stay finite.  256 x 256
+    # x 64 takes the interior loop of every kernel.
+    for M, N, K in ((70, 66, 33), (256, 256, 64)):
+        _overflow_case(variant, M, N, K)
+
+
+def _overflow_case(variant, M, N, K):
     rng = np.random.default_rng(12)
     A = rng.standard_normal((M, K)).astype(np.float32)
     B = rng.standard_normal((K, N)).astype(np.float32)
