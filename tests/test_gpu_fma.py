@@ -245,6 +245,23 @@ def test_fused_gemm_views_and_subnormals():
         assert (rest == 0).all()
 
 
+def test_fused_subnormal_chains_on_interior_tiles():
+    # 256 x 256 x 64 with 16-byte rows: every tile of both kernels takes the
+    # unchecked interior loop.  Products and chains around 2^-126: the fused
+    # step rounds a * b + c once, then the result flushes if it is tiny.
+    M, N, K = 256, 256, 64
+    A = _mat(M, K, 0x9B00)
+    B = _mat(K, N, 0x9B01)
+    A[::3] *= np.float32(2.0 ** -63)
+    B[:, ::2] *= np.float32(2.0 ** -63)
+    A[::5, ::7] = np.float32(2.0 ** -130)
+    ref = oracle.gemm(A, B, fused=True)
+    assert (ref == 0).any() and (np.abs(ref[ref != 0]) < np.float32(2.0 ** -120)).any()
+    for variant in (0, 1):
+        C = br.repro_gemm_fma(to_dev(A), to_dev(B), variant=variant)
+        assert_bitwise(to_host(C), ref, f"interior subnormal chains variant={variant}")
+
+
 def test_fused_forward_workload_full_size_sampled():
     cfg = synth.GEMM
     M, N, K = cfg["M"], cfg["N"], cfg["K"]

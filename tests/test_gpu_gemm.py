@@ -144,14 +144,16 @@ def test_subnormal_operands_and_products(variant):
     # Subnormal inputs read as zero; products below 2^-126 flush; the chain's
     # exact subnormal sums flush.  Compared with the oracle's rule, for every
     # variant (variants 0 and 3 form the products on the matrix cores).
+    # 256 x 256 x 64 takes the unchecked interior loop, 32 x 32 x 40 the
+    # checked one.
     rng = np.random.default_rng(5)
-    M, N, K = 32, 32, 40
-    A = (rng.standard_normal((M, K)) * 2.0 ** -63).astype(np.float32)
-    B = (rng.standard_normal((K, N)) * 2.0 ** -63).astype(np.float32)
-    A[::3, ::2] = np.float32(2.0 ** -130)
-    ref = oracle.gemm(A, B)
-    assert_bitwise(to_host(br.repro_gemm(to_dev(A), to_dev(B), variant=variant)), ref,
-                   f"subnormal products variant={variant}")
+    for M, N, K in ((32, 32, 40), (256, 256, 64)):
+        A = (rng.standard_normal((M, K)) * 2.0 ** -63).astype(np.float32)
+        B = (rng.standard_normal((K, N)) * 2.0 ** -63).astype(np.float32)
+        A[::3, ::2] = np.float32(2.0 ** -130)
+        ref = oracle.gemm(A, B)
+        assert_bitwise(to_host(br.repro_gemm(to_dev(A), to_dev(B), variant=variant)), ref,
+                       f"{M}x{N}x{K} subnormal products variant={variant}")
 
 
 def _boundary_operands(rng, rows, cols):
