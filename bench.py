@@ -47,9 +47,10 @@ FP32_VECTOR_PEAK = 157.3       # TFLOP/s, vendor figure (FMA counted as 2 flops)
 # 78.6 TFLOP/s.  The default GEMM forms the products on the matrix cores
 # (one v_mfma_f32_32x32x1_2b_f32 per 2048 products, 64 busy cycles) and adds
 # them on the VALU; the two units take turns (co-execution counter 0), so per
-# SIMD 2048 MACs cost 64 + 64 cycles, the same 78.6 TFLOP/s ceiling.  Full-rate opcodes (v_mul_f32, v_add_f32, v_xor_b32,
-# v_lshrrev_b32, ...) reach it in either encoding; `bench.py --valu-rates`
-# measures 0.47-0.48 for long streams of them.
+# SIMD 2048 MACs cost 64 + 64 cycles, the same 78.6 TFLOP/s ceiling.
+# Full-rate opcodes (v_mul_f32, v_add_f32, v_xor_b32, v_lshrrev_b32, ...)
+# reach it in either encoding; `bench.py --valu-rates` measures 0.47-0.48 for
+# long streams of them.
 VALU_LANE_OPS = 256 * 128 * 2.4e9
 GEMM_PEAK_TFLOPS = VALU_LANE_OPS / 1e12
 # BLAKE2b: per 128-byte block 12 rounds x 8 G.  The compiled compression
